@@ -1,0 +1,10 @@
+"""MI355X (gfx950) hot path of compressed-KV drafting with lossless verification.
+
+Importing the package loads libvc.so (built in place by ``build.py``) and fails
+loudly if it is missing: every step of the path runs in its HIP kernels.
+"""
+from ._lib import (  # noqa: F401
+    LIB, VcError, Compressed, Tail, FullKV, version, quantize_kv, identity_cache, token_drop_cache,
+    debug_dequant, draft_ws_bytes, draft_attn, verify_ws_bytes, verify_attn, argmax, accept,
+    prefetch_full_kv,
+)

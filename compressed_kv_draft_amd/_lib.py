@@ -1,0 +1,263 @@
+"""ctypes binding of libvc.so: argument marshalling only.
+
+Every computation runs in the HIP kernels of the library; this module turns
+torch tensors into device pointers and the current torch stream into a
+hipStream_t.  If the library is missing the import fails loudly: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libvc.so")
+
+VC_OK = 0
+VC_KV_IDENTITY, VC_KV_QUANT, VC_KV_TOKEN_DROP = 0, 1, 2
+KIND = {"identity": VC_KV_IDENTITY, "quant": VC_KV_QUANT, "token_drop": VC_KV_TOKEN_DROP}
+
+c_int, c_float, c_size, c_void = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+
+class VcKvComp(ctypes.Structure):
+    _fields_ = [("kind", c_int), ("bits", c_int), ("n_quant", c_int),
+                ("k_codes", c_void), ("v_codes", c_void), ("k_meta", c_void), ("v_meta", c_void),
+                ("k_full", c_void), ("v_full", c_void), ("L_full", c_int), ("L_cap", c_int),
+                ("keep_idx", c_void), ("n_keep", c_int)]
+
+
+class VcTail(ctypes.Structure):
+    _fields_ = [("k", c_void), ("v", c_void), ("len", c_void), ("T_cap", c_int)]
+
+
+class VcKvFull(ctypes.Structure):
+    _fields_ = [("k", c_void), ("v", c_void), ("L_cap", c_int), ("page_table", c_void),
+                ("page_tokens", c_int), ("pages_per_seq", c_int), ("n_slots", c_int)]
+
+
+EXPORTS = {
+    # name: (restype, argtypes)
+    "vc_version": (c_int, []),
+    "vc_last_error": (ctypes.c_char_p, []),
+    "vc_quantize_kv": (c_int, [c_void, c_void, c_int, c_int, c_int, c_int, ctypes.POINTER(VcKvComp), c_void]),
+    "vc_debug_dequant": (c_int, [ctypes.POINTER(VcKvComp), c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void]),
+    "vc_draft_ws_bytes": (c_size, [c_int, c_int, c_int, c_int, c_int]),
+    "vc_draft_attn": (c_int, [ctypes.POINTER(VcKvComp), ctypes.POINTER(VcTail), c_void, c_void, c_void,
+                              c_int, c_int, c_int, c_int, c_float, c_void, c_size, c_void]),
+    "vc_verify_ws_bytes": (c_size, [c_int, c_int, c_int, c_int, c_int, c_int]),
+    "vc_verify_attn": (c_int, [c_void, ctypes.POINTER(VcKvFull), c_void, c_int, c_int, c_void,
+                               c_int, c_int, c_int, c_int, c_float, c_void, c_size, c_void]),
+    "vc_argmax": (c_int, [c_void, c_int, c_int, c_void, c_void]),
+    "vc_accept": (c_int, [c_void, c_void, c_int, c_int, c_int, c_void, c_void, c_void]),
+    "vc_prefetch_full_kv": (c_int, [c_void, c_void, c_size, c_int, c_void, c_int, c_int, c_void, c_int,
+                                    c_int, c_int, c_int, c_void, c_void]),
+}
+
+
+class VcError(RuntimeError):
+    pass
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libvc.so not built at {LIB_PATH}; run `python -m compressed_kv_draft_amd.build` "
+                          "(no CPU fallback exists)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in EXPORTS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+LIB = _load()
+
+
+def _check(rc: int, what: str):
+    if rc != VC_OK:
+        msg = LIB.vc_last_error().decode(errors="replace")
+        raise VcError(f"{what} failed ({rc}): {msg}")
+
+
+def _ptr(t):
+    return None if t is None else c_void(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return c_void(s.cuda_stream)
+
+
+def version() -> int:
+    return LIB.vc_version()
+
+
+# ------------------------------------------------------------------ compressor
+
+class Compressed:
+    """Device tensors of one compressed cache plus the C descriptor that points at them."""
+
+    def __init__(self, kind: str, **t):
+        self.kind = kind
+        self.t = t
+        d = VcKvComp()
+        d.kind = KIND[kind]
+        d.bits = int(t.get("bits", 0))
+        d.n_quant = int(t.get("n_quant", 0))
+        for f in ("k_codes", "v_codes", "k_meta", "v_meta", "k_full", "v_full", "keep_idx"):
+            setattr(d, f, _ptr(t.get(f)).value if t.get(f) is not None else None)
+        d.L_full = int(t.get("L_full", 0))
+        d.L_cap = int(t.get("L_cap", 0))
+        d.n_keep = int(t.get("n_keep", 0))
+        self.desc = d
+
+
+def quantize_kv(k_src: torch.Tensor, v_src: torch.Tensor, bits: int, n_quant: int, stream=None) -> Compressed:
+    """k_src/v_src: bf16 [B, Hkv, L_cap, D] on the device.  Returns the QUANT cache."""
+    B, Hkv, L_cap, D = k_src.shape
+    dev = k_src.device
+    rb = D * bits // 8
+    t = dict(bits=bits, n_quant=n_quant,
+             k_codes=torch.empty((B, Hkv, n_quant, rb), dtype=torch.uint8, device=dev),
+             v_codes=torch.empty((B, Hkv, n_quant, rb), dtype=torch.uint8, device=dev),
+             k_meta=torch.empty((B, Hkv, n_quant // 32, D, 2), dtype=torch.float16, device=dev),
+             v_meta=torch.empty((B, Hkv, n_quant, D // 32, 2), dtype=torch.float16, device=dev))
+    comp = Compressed("quant", **t)
+    rc = LIB.vc_quantize_kv(_ptr(k_src), _ptr(v_src), B, Hkv, L_cap, D, ctypes.byref(comp.desc), _stream(stream))
+    _check(rc, "vc_quantize_kv")
+    comp.t["src_keepalive"] = (k_src, v_src)
+    return comp
+
+
+def identity_cache(k_full: torch.Tensor, v_full: torch.Tensor, L_full: int) -> Compressed:
+    return Compressed("identity", k_full=k_full, v_full=v_full, L_full=L_full, L_cap=k_full.shape[2])
+
+
+def token_drop_cache(k_full: torch.Tensor, v_full: torch.Tensor, keep_idx: torch.Tensor) -> Compressed:
+    return Compressed("token_drop", k_full=k_full, v_full=v_full, keep_idx=keep_idx,
+                      n_keep=keep_idx.shape[-1], L_full=k_full.shape[2], L_cap=k_full.shape[2])
+
+
+def debug_dequant(comp: Compressed, B: int, Hkv: int, D: int, b: int, h: int, which: int, stream=None):
+    n = comp.t["n_quant"]
+    out = torch.empty((n, D), dtype=torch.float32, device=comp.t["k_codes"].device)
+    rc = LIB.vc_debug_dequant(ctypes.byref(comp.desc), B, Hkv, D, b, h, which, _ptr(out), _stream(stream))
+    _check(rc, "vc_debug_dequant")
+    return out
+
+
+# ------------------------------------------------------------------ attention
+
+class Tail:
+    def __init__(self, k=None, v=None, lens=None):
+        self.k, self.v, self.lens = k, v, lens
+        d = VcTail()
+        if k is not None:
+            d.k, d.v, d.len = k.data_ptr(), v.data_ptr(), lens.data_ptr()
+            d.T_cap = k.shape[2]
+        else:
+            d.T_cap = 0
+        self.desc = d
+
+
+def draft_ws_bytes(B, Hq, Hkv, D, max_keys) -> int:
+    return int(LIB.vc_draft_ws_bytes(B, Hq, Hkv, D, max_keys))
+
+
+def draft_attn(comp: Compressed, tail: Tail, q: torch.Tensor, scale: float, out=None, lse=None, ws=None,
+               Hkv: int | None = None, stream=None):
+    """q: bf16 [B, Hq, D].  Returns fp32 [B, Hq, D]."""
+    B, Hq, D = q.shape
+    if Hkv is None:
+        ref = comp.t.get("k_codes") if comp.kind == "quant" else comp.t.get("k_full")
+        Hkv = ref.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if ws is None:
+        n_main = comp.t.get("n_quant", 0) if comp.kind == "quant" else (
+            comp.t.get("n_keep", 0) if comp.kind == "token_drop" else comp.t.get("L_full", 0))
+        need = draft_ws_bytes(B, Hq, Hkv, D, n_main + tail.desc.T_cap)
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    rc = LIB.vc_draft_attn(ctypes.byref(comp.desc), ctypes.byref(tail.desc), _ptr(q), _ptr(out), _ptr(lse),
+                           B, Hq, Hkv, D, float(scale), _ptr(ws), ws.numel(), _stream(stream))
+    _check(rc, "vc_draft_attn")
+    return out
+
+
+class FullKV:
+    def __init__(self, k, v=None, L_cap=0, page_table=None, page_tokens=0, pages_per_seq=0, n_slots=0):
+        self.k, self.v, self.page_table = k, v, page_table
+        d = VcKvFull()
+        d.k = k.data_ptr()
+        d.v = v.data_ptr() if v is not None else None
+        d.L_cap = int(L_cap)
+        d.page_table = page_table.data_ptr() if page_table is not None else None
+        d.page_tokens = int(page_tokens)
+        d.pages_per_seq = int(pages_per_seq)
+        d.n_slots = int(n_slots)
+        self.desc = d
+
+
+def verify_ws_bytes(B, Hq, Hkv, D, n_q, max_ctx) -> int:
+    return int(LIB.vc_verify_ws_bytes(B, Hq, Hkv, D, n_q, max_ctx))
+
+
+def verify_attn(q: torch.Tensor, kv: FullKV, ctx_len: torch.Tensor, max_ctx: int, Hkv: int, scale: float,
+                out=None, ws=None, stream=None):
+    """q: bf16 [B, Hq, n_q, D].  Returns fp32 [B, Hq, n_q, D]."""
+    B, Hq, n_q, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, n_q, D), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = torch.empty(verify_ws_bytes(B, Hq, Hkv, D, n_q, max_ctx), dtype=torch.uint8, device=q.device)
+    rc = LIB.vc_verify_attn(_ptr(q), ctypes.byref(kv.desc), _ptr(ctx_len), int(max_ctx), n_q, _ptr(out),
+                            B, Hq, Hkv, D, float(scale), _ptr(ws), ws.numel(), _stream(stream))
+    _check(rc, "vc_verify_attn")
+    return out
+
+
+# ------------------------------------------------------------------ tokens
+
+def argmax(logits: torch.Tensor, ids=None, stream=None):
+    rows, V = logits.reshape(-1, logits.shape[-1]).shape
+    if ids is None:
+        ids = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    _check(LIB.vc_argmax(_ptr(logits), rows, V, _ptr(ids), _stream(stream)), "vc_argmax")
+    return ids
+
+
+def accept(draft_ids: torch.Tensor, verify_logits: torch.Tensor, out_ids=None, n_accept=None, stream=None):
+    """draft_ids int32 [B, k]; verify_logits fp32 [B, k+1, V]."""
+    B, k1, V = verify_logits.shape
+    k = k1 - 1
+    if out_ids is None:
+        out_ids = torch.empty((B, k1), dtype=torch.int32, device=verify_logits.device)
+    if n_accept is None:
+        n_accept = torch.empty(B, dtype=torch.int32, device=verify_logits.device)
+    rc = LIB.vc_accept(_ptr(draft_ids), _ptr(verify_logits), B, k, V, _ptr(out_ids), _ptr(n_accept),
+                       _stream(stream))
+    _check(rc, "vc_accept")
+    return out_ids, n_accept
+
+
+# ------------------------------------------------------------------ prefetch
+
+def prefetch_full_kv(host_pool: torch.Tensor, dev_pool: torch.Tensor, page_bytes: int, page_table_host,
+                     seq_ids, tok_begin: int, tok_end: int, page_tokens: int, stream=None, done_event=None):
+    """host_pool: pinned CPU uint8 [slots * page_bytes]; page_table_host: int32 numpy [n_seq, pages]."""
+    import numpy as np
+    tab = np.ascontiguousarray(page_table_host, dtype=np.int32)
+    seqs = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int32))
+    n_slots = dev_pool.numel() // page_bytes
+    if host_pool.numel() < n_slots * page_bytes:
+        raise VcError(f"host pool holds {host_pool.numel()} bytes < {n_slots} slots * {page_bytes}")
+    ev = c_void(done_event.cuda_event) if done_event is not None else None
+    s = torch.cuda.current_stream() if stream is None else stream
+    rc = LIB.vc_prefetch_full_kv(c_void(host_pool.data_ptr()), _ptr(dev_pool), page_bytes, n_slots,
+                                 tab.ctypes.data_as(c_void), tab.shape[0], tab.shape[1],
+                                 seqs.ctypes.data_as(c_void), len(seqs), tok_begin, tok_end, page_tokens,
+                                 c_void(s.cuda_stream), ev)
+    _check(rc, "vc_prefetch_full_kv")

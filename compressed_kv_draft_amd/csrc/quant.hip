@@ -1,0 +1,194 @@
+// KIVI-style asymmetric group quantiser for the lossy draft cache, and a
+// dequantising read-back used to check it bit for bit.
+//
+// [VC Problem Statement: token dropping and quantisation are the lossy KV
+//  compressors; VC Architecture Support: KIVI behind the uniform interface]
+// The page gives no formula; the quantiser is the plain min/max one, every
+// step an IEEE fp32 operation with round-to-nearest-even (no contraction).
+#include "vc_common.h"
+
+namespace vc {
+namespace {
+
+struct alignas(4) H2 {
+  _Float16 s, z;
+};
+
+// One group's scale/zero: s = f16((mx - mn) / qmax), z = f16(mn).
+__device__ __forceinline__ void group_params(float mn, float mx, int qmax, _Float16& sh, _Float16& zh) {
+#pragma clang fp contract(off)
+  float s32 = (mx - mn) / (float)qmax;  // correctly rounded division (no fast-math)
+  sh = (_Float16)s32;
+  zh = (_Float16)mn;
+}
+
+__device__ __forceinline__ uint32_t code_of(float x, float s, float z, int qmax) {
+#pragma clang fp contract(off)
+  if (s == 0.0f) return 0u;
+  float t = (x - z) / s;
+  float r = rintf(t);
+  r = fminf(fmaxf(r, 0.0f), (float)qmax);
+  return (uint32_t)r;
+}
+
+// K: groups of 32 tokens of one channel.  One thread per (32-token block, byte
+// column): it owns the 8/bits channels packed into that byte.
+template <int BITS>
+__global__ void quant_k_kernel(const uint16_t* __restrict__ src, int L_cap, int D, int n_quant,
+                               uint8_t* __restrict__ codes, H2* __restrict__ meta) {
+  constexpr int PER = 8 / BITS;
+  constexpr int QMAX = (1 << BITS) - 1;
+  const int unit = blockIdx.y;
+  const int blk = blockIdx.x;
+  const int col = threadIdx.x;  // byte column
+  const int row_bytes = D * BITS / 8;
+  if (col >= row_bytes) return;
+  const uint16_t* base = src + ((size_t)unit * L_cap + (size_t)blk * 32) * D;
+  uint32_t packed[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) packed[i] = 0;
+  for (int e = 0; e < PER; ++e) {
+    const int d = col * PER + e;
+    float x[32];
+    float mn, mx;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = bf16_to_f32(base[(size_t)i * D + d]);
+    mn = x[0];
+    mx = x[0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) {
+      mn = fminf(mn, x[i]);
+      mx = fmaxf(mx, x[i]);
+    }
+    _Float16 sh, zh;
+    group_params(mn, mx, QMAX, sh, zh);
+    const float s = (float)sh, z = (float)zh;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) packed[i] |= code_of(x[i], s, z, QMAX) << (BITS * e);
+    H2 m;
+    m.s = sh;
+    m.z = zh;
+    meta[((size_t)unit * (n_quant / 32) + blk) * D + d] = m;
+  }
+  uint8_t* out = codes + ((size_t)unit * n_quant + (size_t)blk * 32) * row_bytes + col;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) out[(size_t)i * row_bytes] = (uint8_t)packed[i];
+}
+
+// V: groups of 32 channels of one token.  One thread per (token, group).
+template <int BITS>
+__global__ void quant_v_kernel(const uint16_t* __restrict__ src, int L_cap, int D, int n_quant,
+                               uint8_t* __restrict__ codes, H2* __restrict__ meta) {
+  constexpr int QMAX = (1 << BITS) - 1;
+  const int unit = blockIdx.y;
+  const int G = D / 32;
+  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= n_quant * G) return;
+  const int t = gid / G, grp = gid % G;
+  const uint16_t* row = src + ((size_t)unit * L_cap + t) * D + grp * 32;
+  float x[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) x[i] = bf16_to_f32(row[i]);
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 32; ++i) {
+    mn = fminf(mn, x[i]);
+    mx = fmaxf(mx, x[i]);
+  }
+  _Float16 sh, zh;
+  group_params(mn, mx, QMAX, sh, zh);
+  const float s = (float)sh, z = (float)zh;
+  const int row_bytes = D * BITS / 8;
+  uint8_t* out = codes + ((size_t)unit * n_quant + t) * row_bytes + grp * 32 * BITS / 8;
+  constexpr int PER = 8 / BITS;
+#pragma unroll
+  for (int byte = 0; byte < 32 / PER; ++byte) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) v |= code_of(x[byte * PER + e], s, z, QMAX) << (BITS * e);
+    out[byte] = (uint8_t)v;
+  }
+  H2 m;
+  m.s = sh;
+  m.z = zh;
+  meta[((size_t)unit * n_quant + t) * G + grp] = m;
+}
+
+__device__ __forceinline__ uint32_t unpack_code(const uint8_t* row, int d, int bits) {
+  if (bits == 4) return (row[d >> 1] >> ((d & 1) * 4)) & 15u;
+  return (row[d >> 2] >> ((d & 3) * 2)) & 3u;
+}
+
+__global__ void dequant_kernel(const uint8_t* __restrict__ codes, const H2* __restrict__ meta, int bits,
+                               int n_quant, int D, int which, float* __restrict__ out) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n_quant * D) return;
+  const int t = idx / D, d = idx % D;
+  const int row_bytes = D * bits / 8;
+  const uint32_t c = unpack_code(codes + (size_t)t * row_bytes, d, bits);
+  const H2 m = which == 0 ? meta[(size_t)(t / 32) * D + d] : meta[(size_t)t * (D / 32) + d / 32];
+  out[idx] = fmaf((float)c, (float)m.s, (float)m.z);
+}
+
+}  // namespace
+}  // namespace vc
+
+using namespace vc;
+
+extern "C" int vc_quantize_kv(const void* k_src, const void* v_src, int B, int Hkv, int L_cap, int D,
+                              const vc_kv_comp* out, hipStream_t stream) {
+  VC_CHECK(out != nullptr, "vc_quantize_kv: out descriptor is NULL");
+  VC_CHECK(out->kind == VC_KV_QUANT, "vc_quantize_kv: out->kind must be VC_KV_QUANT");
+  VC_CHECK(out->bits == 2 || out->bits == 4, "vc_quantize_kv: bits must be 2 or 4 (got %d)", out->bits);
+  VC_CHECK(B > 0 && Hkv > 0 && L_cap > 0, "vc_quantize_kv: bad B/Hkv/L_cap (%d,%d,%d)", B, Hkv, L_cap);
+  if (D != 64 && D != 128) return fail(VC_ERR_UNSUPPORTED, "vc_quantize_kv: D=%d not in {64,128}", D);
+  const int nq = out->n_quant;
+  VC_CHECK(nq >= 0 && nq % 32 == 0 && nq <= L_cap, "vc_quantize_kv: n_quant=%d must be a multiple of 32 <= L_cap", nq);
+  VC_CHECK(k_src && v_src && out->k_codes && out->v_codes && out->k_meta && out->v_meta,
+           "vc_quantize_kv: null pointer");
+  VC_CHECK(aligned(k_src, 2) && aligned(v_src, 2) && aligned(out->k_meta, 4) && aligned(out->v_meta, 4),
+           "vc_quantize_kv: misaligned pointer");
+  if (nq == 0) return VC_OK;
+  const int units = B * Hkv;
+  uint8_t* kc = const_cast<uint8_t*>(out->k_codes);
+  uint8_t* vcodes = const_cast<uint8_t*>(out->v_codes);
+  H2* km = reinterpret_cast<H2*>(const_cast<void*>(out->k_meta));
+  H2* vm = reinterpret_cast<H2*>(const_cast<void*>(out->v_meta));
+  const uint16_t* ks = static_cast<const uint16_t*>(k_src);
+  const uint16_t* vs = static_cast<const uint16_t*>(v_src);
+  dim3 gk(nq / 32, units);
+  const int cols = D * out->bits / 8;
+  const int G = D / 32;
+  dim3 gv((nq * G + 255) / 256, units);
+  if (out->bits == 4) {
+    quant_k_kernel<4><<<gk, cols, 0, stream>>>(ks, L_cap, D, nq, kc, km);
+    quant_v_kernel<4><<<gv, 256, 0, stream>>>(vs, L_cap, D, nq, vcodes, vm);
+  } else {
+    quant_k_kernel<2><<<gk, cols, 0, stream>>>(ks, L_cap, D, nq, kc, km);
+    quant_v_kernel<2><<<gv, 256, 0, stream>>>(vs, L_cap, D, nq, vcodes, vm);
+  }
+  VC_HIP(hipGetLastError());
+  return VC_OK;
+}
+
+extern "C" int vc_debug_dequant(const vc_kv_comp* comp, int B, int Hkv, int D, int b, int h, int which,
+                                float* out, hipStream_t stream) {
+  VC_CHECK(comp && out, "vc_debug_dequant: null pointer");
+  VC_CHECK(comp->kind == VC_KV_QUANT, "vc_debug_dequant: kind must be VC_KV_QUANT");
+  VC_CHECK(comp->bits == 2 || comp->bits == 4, "vc_debug_dequant: bits must be 2 or 4");
+  if (D != 64 && D != 128) return fail(VC_ERR_UNSUPPORTED, "vc_debug_dequant: D=%d not in {64,128}", D);
+  VC_CHECK(b >= 0 && b < B && h >= 0 && h < Hkv && (which == 0 || which == 1), "vc_debug_dequant: bad index");
+  const int nq = comp->n_quant;
+  VC_CHECK(nq >= 0 && nq % 32 == 0, "vc_debug_dequant: bad n_quant");
+  if (nq == 0) return VC_OK;
+  const size_t unit = (size_t)b * Hkv + h;
+  const int row_bytes = D * comp->bits / 8;
+  const uint8_t* codes = (which == 0 ? comp->k_codes : comp->v_codes) + unit * nq * row_bytes;
+  const H2* meta = reinterpret_cast<const H2*>(which == 0 ? comp->k_meta : comp->v_meta);
+  meta += which == 0 ? unit * (nq / 32) * D : unit * nq * (D / 32);
+  VC_CHECK(codes && meta, "vc_debug_dequant: null codes/meta");
+  const int n = nq * D;
+  dequant_kernel<<<(n + 255) / 256, 256, 0, stream>>>(codes, meta, comp->bits, nq, D, which, out);
+  VC_HIP(hipGetLastError());
+  return VC_OK;
+}

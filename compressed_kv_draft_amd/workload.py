@@ -1,0 +1,135 @@
+"""Device state of one single-layer draft/verify workload (harness glue).
+
+Lays the seeded synthetic inputs out in device memory in the layouts the C ABI
+expects and runs the GPU compressor (vc_quantize_kv) for the draft cache.  Used
+by the benchmark and the GPU tests; holds no attention arithmetic.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from synth import inputs as I
+from synth.configs import Workload
+
+from . import _lib as vc
+
+
+def bf16_dev(bits: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def paged_pool(w: Workload, k_all: np.ndarray, v_all: np.ndarray, table: np.ndarray, n_slots: int) -> np.ndarray:
+    """Pool [n_slots, Hkv, 2, page, D] (bf16 bits) holding rows [0, L + n_q) of every sequence."""
+    pt = w.page_tokens
+    P = table.shape[1]
+    n = w.L + w.n_q
+    pool = np.zeros((n_slots, w.Hkv, 2, pt, w.D), dtype=np.uint16)
+    pad = P * pt - n
+    for b in range(w.B):
+        kb = np.pad(k_all[b], ((0, 0), (0, pad), (0, 0))).reshape(w.Hkv, P, pt, w.D)
+        vb = np.pad(v_all[b], ((0, 0), (0, pad), (0, 0))).reshape(w.Hkv, P, pt, w.D)
+        pool[table[b], :, 0] = kb.transpose(1, 0, 2, 3)
+        pool[table[b], :, 1] = vb.transpose(1, 0, 2, 3)
+    return pool
+
+
+class DeviceWorkload:
+    """All inputs of one round on the device.
+
+    full_k/full_v  bf16 [B, Hkv, L + n_q, D]: context then the n_q new rows
+    comp           the draft cache (quant / token_drop / identity)
+    tail           exact rows of the draft: recent window then new rows
+    tail_lens[j]   int32 [B] tail length of draft step j (window + j + 1)
+    q_steps[j]     bf16 [B, Hq, D] query of draft step j; q_verify [B, Hq, n_q, D]
+    """
+
+    def __init__(self, w: Workload, device="cuda", Q: np.ndarray | None = None, with_vocab: bool = True,
+                 ctx=None):
+        self.w = w
+        self.device = device
+        g = w.g
+        if ctx is None:
+            K = I.context_kv(w, "k")
+            V = I.context_kv(w, "v")
+        else:
+            K, V = ctx
+        Kn = I.new_rows(w, "k")
+        Vn = I.new_rows(w, "v")
+        if Q is None:
+            Q = I.queries(w)
+        self.np = dict(K=K, V=V, Kn=Kn, Vn=Vn, Q=Q)
+        k_all = np.concatenate([K, Kn], axis=2)
+        v_all = np.concatenate([V, Vn], axis=2)
+        self.L_cap = w.L + w.n_q
+        self.paged = w.paged
+        if w.paged:
+            table, n_slots = I.page_table(w)
+            self.page_table_np = table
+            self.n_slots = n_slots
+            pool = paged_pool(w, k_all, v_all, table, n_slots)
+            self.pool_np = pool
+            self.pool = torch.from_numpy(pool.view(np.int16)).to(device).view(torch.bfloat16)
+            self.page_table = torch.from_numpy(table).to(device)
+            self.full = vc.FullKV(self.pool, None, 0, self.page_table, w.page_tokens, table.shape[1], n_slots)
+        self.full_k = bf16_dev(k_all, device)
+        self.full_v = bf16_dev(v_all, device)
+        if not w.paged:
+            self.full = vc.FullKV(self.full_k, self.full_v, L_cap=self.L_cap)
+        del k_all, v_all
+        self.ctx_len = torch.full((w.B,), w.L, dtype=torch.int32, device=device)
+        # draft cache
+        if w.kind == "quant":
+            self.comp = vc.quantize_kv(self.full_k, self.full_v, w.bits, w.n_quant)
+            R = w.residual
+            tk = np.concatenate([K[:, :, w.L - R:w.L], Kn], axis=2)
+            tv = np.concatenate([V[:, :, w.L - R:w.L], Vn], axis=2)
+        elif w.kind == "token_drop":
+            self.keep_np = I.keep_indices(w)
+            self.keep = torch.from_numpy(self.keep_np).to(device)
+            self.comp = vc.token_drop_cache(self.full_k, self.full_v, self.keep)
+            R = 0
+            tk, tv = Kn, Vn
+        else:
+            self.comp = vc.identity_cache(self.full_k, self.full_v, w.L)
+            R = 0
+            tk, tv = Kn, Vn
+        self.tail_k = bf16_dev(tk, device)
+        self.tail_v = bf16_dev(tv, device)
+        self.tail_lens = [torch.full((w.B,), R + j + 1, dtype=torch.int32, device=device) for j in range(w.k)]
+        self.tails = [vc.Tail(self.tail_k, self.tail_v, tl) for tl in self.tail_lens]
+        self.q_verify = bf16_dev(Q, device)
+        self.q_steps = [self.q_verify[:, :, j, :].contiguous() for j in range(w.k)]
+        self.scale = float(np.float32(1.0 / np.sqrt(w.D)))
+        self.n_main = {"quant": w.n_quant, "token_drop": w.n_keep, "identity": w.L}[w.kind]
+        self.draft_ws = torch.empty(vc.draft_ws_bytes(w.B, w.Hq, w.Hkv, w.D, self.n_main + R + w.n_q),
+                                    dtype=torch.uint8, device=device)
+        self.verify_ws = torch.empty(vc.verify_ws_bytes(w.B, w.Hq, w.Hkv, w.D, w.n_q, w.L),
+                                     dtype=torch.uint8, device=device)
+        self.draft_out = torch.empty((w.k, w.B, w.Hq, w.D), dtype=torch.float32, device=device)
+        self.verify_out = torch.empty((w.B, w.Hq, w.n_q, w.D), dtype=torch.float32, device=device)
+        self.W = None
+        if with_vocab:
+            self.W = torch.from_numpy(I.vocab_matrix(w)).to(device)
+
+    # one round of the path -------------------------------------------------
+    def draft_step(self, j: int, stream=None):
+        w = self.w
+        return vc.draft_attn(self.comp, self.tails[j], self.q_steps[j], self.scale, out=self.draft_out[j],
+                             ws=self.draft_ws, Hkv=w.Hkv, stream=stream)
+
+    def verify(self, stream=None):
+        w = self.w
+        return vc.verify_attn(self.q_verify, self.full, self.ctx_len, w.L, w.Hkv, self.scale,
+                              out=self.verify_out, ws=self.verify_ws, stream=stream)
+
+    def draft_logits(self):
+        """[B, k, V] logits of the drafts (harness glue: fp32 GEMM in torch)."""
+        w = self.w
+        o = self.draft_out.permute(1, 0, 2, 3).reshape(w.B, w.k, w.Hq * w.D)
+        return torch.matmul(o, self.W)
+
+    def verify_logits(self):
+        w = self.w
+        o = self.verify_out.permute(0, 2, 1, 3).reshape(w.B, w.n_q, w.Hq * w.D)
+        return torch.matmul(o, self.W).contiguous()

@@ -1,0 +1,236 @@
+/*
+ * vc.h — C ABI of libvc.so, the gfx950 (MI355X) hot path of compressed-KV
+ * drafting with lossless verification.
+ *
+ * Source of the method: "VeriCache: Turning Lossy KV Cache into Lossless LLM
+ * Inference" (gist.science explainer of the paper, English and Korean pages).
+ * Each entry point below names the section of that page that defines the
+ * operation.  The pages describe the method in prose only; every layout,
+ * precision and error rule here is this library's own.
+ *
+ * Conventions shared by all entry points
+ *  - Return value: VC_OK (0) or a negative VC_ERR_* code.  vc_last_error()
+ *    returns a thread-local message for the last failure on this thread.
+ *  - Every argument is validated on the host before anything is enqueued; a
+ *    rejected call enqueues nothing.  Device-side faults surface as
+ *    VC_ERR_HIP from a later call or from the caller's own synchronisation.
+ *  - Pointers marked "device" must be device memory on the current HIP device;
+ *    "host" pointers are read during the call only.  The caller owns every
+ *    buffer; the library never allocates, frees or retains device memory.
+ *  - Calls are asynchronous on the given stream and never synchronise.  They
+ *    are reentrant; two calls that share a workspace must be stream-ordered.
+ *  - bf16 = IEEE bfloat16 bit patterns; f16 = IEEE binary16; all tensors are
+ *    dense row-major with the shapes given.
+ *  - Heads: query head h reads KV head h / (Hq / Hkv) (contiguous GQA groups).
+ */
+#ifndef VC_H_
+#define VC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VC_OK 0
+#define VC_ERR_INVALID -1     /* bad shape, null or misaligned pointer, bad enum */
+#define VC_ERR_UNSUPPORTED -2 /* valid but not built (e.g. head_dim not in {64, 128}) */
+#define VC_ERR_HIP -3         /* a HIP runtime call failed */
+#define VC_ERR_WORKSPACE -4   /* workspace smaller than the matching *_ws_bytes() */
+
+/* ------------------------------------------------------------------------ */
+/* Uniform compressor interface                                              */
+/* [VC Architecture Support: one compressor interface for token-dropping and */
+/*  quantisation methods; VC Core Algorithm: drafting reads KV_comp]         */
+/* ------------------------------------------------------------------------ */
+
+#define VC_KV_IDENTITY 0   /* no compression: all L_full context rows      */
+#define VC_KV_QUANT 1      /* asymmetric b-bit groups of 32 (KIVI-style)   */
+#define VC_KV_TOKEN_DROP 2 /* a kept subset of context rows, by index      */
+
+/*
+ * QUANT layout (per (b, kv-head) slices are dense and consecutive):
+ *   k_codes  u8 [B][Hkv][n_quant][D*bits/8]  codes of token t packed along D:
+ *            4-bit: channel 2i in the low nibble of byte i, 2i+1 in the high
+ *            nibble; 2-bit: channel i at bit 2*(i%4) of byte i/4.
+ *   v_codes  u8 [B][Hkv][n_quant][D*bits/8]  same packing.
+ *   k_meta   f16x2 [B][Hkv][n_quant/32][D]   {scale, zero} of the group formed
+ *            by 32 consecutive tokens of one channel.
+ *   v_meta   f16x2 [B][Hkv][n_quant][D/32]   {scale, zero} of the group formed
+ *            by 32 consecutive channels of one token.
+ *   Dequantised value = fp32(code * scale + zero), a single rounding.
+ * IDENTITY / TOKEN_DROP read k_full / v_full  bf16 [B][Hkv][L_cap][D]; rows
+ *   [0, L_full) are context.  keep_idx int32 [B][Hkv][n_keep], sorted,
+ *   each in [0, L_full); out-of-range entries are skipped, not dereferenced.
+ * All pointers are device pointers; unused ones may be NULL.
+ */
+typedef struct vc_kv_comp {
+  int kind;          /* VC_KV_*                                    */
+  int bits;          /* QUANT: 2 or 4                              */
+  int n_quant;       /* QUANT: quantised context rows, % 32 == 0   */
+  const uint8_t* k_codes;
+  const uint8_t* v_codes;
+  const void* k_meta;
+  const void* v_meta;
+  const void* k_full;
+  const void* v_full;
+  int L_full;        /* IDENTITY: context rows                     */
+  int L_cap;         /* IDENTITY/TOKEN_DROP: row capacity of k_full */
+  const int32_t* keep_idx;
+  int n_keep;        /* TOKEN_DROP: kept rows per (b, kv-head)      */
+} vc_kv_comp;
+
+/*
+ * Exact rows every draft step also attends to, after the compressed part:
+ * the uncompressed recent window followed by the rows of this round's drafted
+ * positions up to and including the current one.
+ *   k, v  device bf16 [B][Hkv][T_cap][D];  len device int32 [B], each clamped
+ *   to [0, T_cap].  T_cap may be 0 (then k, v, len may be NULL).
+ */
+typedef struct vc_tail {
+  const void* k;
+  const void* v;
+  const int32_t* len;
+  int T_cap;
+} vc_tail;
+
+/*
+ * Full (exact) cache for verification.
+ *  Contiguous (page_table == NULL): k, v device bf16 [B][Hkv][L_cap][D].
+ *  Paged: k = device pool base; v unused.  A page holds page_tokens tokens of
+ *   every KV head as bf16 [Hkv][2 (K then V)][page_tokens][D]; logical page p
+ *   of sequence b sits in slot page_table[b * pages_per_seq + p] (device
+ *   int32).  page_tokens is a power of two >= 8; the pool holds n_slots
+ *   pages, and a slot outside [0, n_slots) reads as zeros, never out of
+ *   bounds.
+ */
+typedef struct vc_kv_full {
+  const void* k;
+  const void* v;
+  int L_cap;
+  const int32_t* page_table;
+  int page_tokens;
+  int pages_per_seq;
+  int n_slots;
+} vc_kv_full;
+
+/* ------------------------------------------------------------------------ */
+
+int vc_version(void);
+const char* vc_last_error(void);
+
+/*
+ * vc_quantize_kv — build the QUANT cache from bf16 rows [0, n_quant) of
+ * k_src / v_src (device bf16 [B][Hkv][L_cap][D]).  [VC Problem Statement:
+ * quantisation as a lossy KV compressor; VC Architecture Support: KIVI]
+ * Per group: mn/mx exact; s = f16((mx - mn) / (2^bits - 1)) and z = f16(mn)
+ * (fp32 subtract and divide, round-to-nearest-even); code = 0 if s == 0, else
+ * clamp(rint((x - z) / s), 0, 2^bits - 1) in fp32.  Writes the QUANT layout
+ * above (out->k_codes etc. are written through; kind/bits/n_quant are read).
+ * D in {64, 128}; bits in {2, 4}; n_quant % 32 == 0, n_quant <= L_cap.
+ */
+int vc_quantize_kv(const void* k_src, const void* v_src, int B, int Hkv, int L_cap, int D,
+                   const vc_kv_comp* out, hipStream_t stream);
+
+/*
+ * vc_debug_dequant — dequantised K (which = 0) or V (which = 1) of one
+ * (b, kv-head) as fp32 [n_quant][D] into out (device).  For bit-exact checks.
+ */
+int vc_debug_dequant(const vc_kv_comp* comp, int B, int Hkv, int D, int b, int h, int which,
+                     float* out, hipStream_t stream);
+
+/*
+ * vc_draft_attn — one draft decode step.  [VC Core Algorithm: drafting
+ * generates candidate tokens with the compressed cache KV_comp; VC Key System
+ * Innovations P1: drafting is HBM-bandwidth bound]
+ * For every (b, h): o = softmax(scale * q K^T) V over the compressed context
+ * rows of KV head h/(Hq/Hkv) followed by the tail rows [0, tail.len[b]).
+ *   q    device bf16 [B][Hq][D]
+ *   out  device fp32 [B][Hq][D]
+ *   lse  device fp32 [B][Hq] or NULL: natural log of sum_t exp(scale q.k_t)
+ *   ws   device workspace of at least vc_draft_ws_bytes(B, Hq, Hkv, D,
+ *        max keys) bytes, 256-byte aligned.  A sequence with no key at all
+ *        gets o = 0 and lse = -inf.
+ * D in {64, 128}; Hq % Hkv == 0; Hq / Hkv <= 8.
+ */
+size_t vc_draft_ws_bytes(int B, int Hq, int Hkv, int D, int max_keys);
+int vc_draft_attn(const vc_kv_comp* comp, const vc_tail* tail, const void* q, float* out,
+                  float* lse, int B, int Hq, int Hkv, int D, float scale, void* ws,
+                  size_t ws_bytes, hipStream_t stream);
+
+/*
+ * vc_verify_attn — causal verification of n_q positions in one pass.
+ * [VC Core Algorithm: a single forward pass with KV_full verifies all drafted
+ * tokens in parallel; VC Key System Innovations P1: verification is
+ * interconnect- and compute-bound]
+ * Position j of sequence b (query q[b][h][j]) attends to keys [0,
+ * ctx_len[b] + j] of the full cache: the context and the new rows of the
+ * positions up to and including j, which the caller wrote at rows
+ * ctx_len[b] .. ctx_len[b] + n_q - 1 beforehand.  Also serves as prefill
+ * (ctx_len = 0, large n_q).
+ *   q        device bf16 [B][Hq][n_q][D]
+ *   ctx_len  device int32 [B]; each must be <= max_ctx (host int) and
+ *            ctx_len + n_q must fit the cache (L_cap or pages_per_seq pages).
+ *   out      device fp32 [B][Hq][n_q][D]
+ *   ws       device workspace of at least vc_verify_ws_bytes(...) bytes.
+ * Precision: q.k products on bf16 matrix cores with fp32 accumulation; the
+ * softmax in fp32; probabilities rounded to f16 (nearest even) and values
+ * converted bf16 -> f16 for the P.V product (fp32 accumulation).  Values must
+ * lie in the f16 range (|v| < 65504).
+ * D in {64, 128}; Hq % Hkv == 0.
+ */
+size_t vc_verify_ws_bytes(int B, int Hq, int Hkv, int D, int n_q, int max_ctx);
+int vc_verify_attn(const void* q, const vc_kv_full* kv, const int32_t* ctx_len, int max_ctx,
+                   int n_q, float* out, int B, int Hq, int Hkv, int D, float scale, void* ws,
+                   size_t ws_bytes, hipStream_t stream);
+
+/*
+ * vc_argmax — greedy token of each row: ids[r] = index of the largest of
+ * logits[r][0..V) (device fp32 [rows][V]); ties go to the lowest index.
+ * Rows containing NaN give an unspecified index in [0, V).
+ */
+int vc_argmax(const float* logits, int rows, int V, int32_t* ids, hipStream_t stream);
+
+/*
+ * vc_accept — greedy acceptance.  [VC Core Algorithm: tokens are accepted up
+ * to the first mismatch; if all drafts match, a bonus token is accepted; the
+ * loop repeats from the last accepted token]
+ *   draft_ids      device int32 [B][k]      d_0 .. d_{k-1}
+ *   verify_logits  device fp32 [B][k+1][V]  logits of verify positions 0..k
+ *   out_ids        device int32 [B][k+1]    d_0..d_{n-1}, y_n, then -1
+ *   n_accept       device int32 [B]         n = first j < k with d_j != y_j,
+ *                                           else k;  y_j = argmax (lowest
+ *                                           index on ties) of position j
+ * The emitted count is n + 1: at a mismatch the verifier's token replaces the
+ * rejected draft.  k >= 0 (k = 0 emits the single verifier token).
+ */
+int vc_accept(const int32_t* draft_ids, const float* verify_logits, int B, int k, int V,
+              int32_t* out_ids, int32_t* n_accept, hipStream_t stream);
+
+/*
+ * vc_prefetch_full_kv — stream the full-KV pages of tokens [tok_begin,
+ * tok_end) of the listed sequences from a pinned host pool into the device
+ * pool, as host-to-device DMA copies on copy_stream, then record `done` (if
+ * not NULL) on copy_stream.  [VC Architecture Support: long-context decoding
+ * keeps the full KV in CPU memory and loads it over PCIe for verification;
+ * VC Key System Innovations P1: the load overlaps other requests' drafting]
+ *   host_pool  pinned host memory (hipHostMalloc), slots * page_bytes bytes
+ *   dev_pool   device memory of the same slot layout
+ *   page_table host int32 [n_seq_total][pages_per_seq]; slot of logical page
+ *              p of sequence b (same slot in both pools); slots < n_slots
+ *   seq_ids    host int32 [n_seq]
+ * Pages p in [tok_begin / page_tokens, ceil(tok_end / page_tokens)) are copied;
+ * runs of consecutive slots are merged into one copy.  No kernels run.
+ * An unpinned host_pool is rejected with VC_ERR_INVALID.
+ */
+int vc_prefetch_full_kv(const void* host_pool, void* dev_pool, size_t page_bytes, int n_slots,
+                        const int32_t* page_table, int n_seq_total, int pages_per_seq,
+                        const int32_t* seq_ids, int n_seq, int tok_begin, int tok_end,
+                        int page_tokens, hipStream_t copy_stream, hipEvent_t done);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VC_H_ */

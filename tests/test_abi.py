@@ -1,0 +1,76 @@
+"""The C-ABI library builds, loads and exports every symbol include/vc.h declares
+(no compute: these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "compressed_kv_draft_amd", "libvc.so")
+HDR = os.path.join(ROOT, "include", "vc.h")
+
+
+def declared_functions():
+    src = open(HDR).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(vc_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("vc_draft_attn", "vc_verify_attn", "vc_accept", "vc_prefetch_full_kv",
+                 "vc_quantize_kv", "vc_debug_dequant", "vc_argmax", "vc_draft_ws_bytes",
+                 "vc_verify_ws_bytes", "vc_last_error", "vc_version"):
+        assert want in names, want
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libvc.so is not built (run __graft_entry__.build())")
+    return ctypes.CDLL(LIB)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_covers_the_header():
+    # the Python binding declares argtypes for every C entry point (parsed, not imported:
+    # importing it would need a GPU runtime)
+    src = open(os.path.join(ROOT, "compressed_kv_draft_amd", "_lib.py")).read()
+    for n in declared_functions():
+        assert f'"{n}"' in src, n
+
+
+def test_host_validation_without_gpu(lib):
+    """Argument checks run on the host before anything is enqueued."""
+    lib.vc_last_error.restype = ctypes.c_char_p
+    lib.vc_version.restype = ctypes.c_int
+    assert lib.vc_version() >= 1
+    f = lib.vc_draft_attn
+    f.restype = ctypes.c_int
+    rc = f(None, None, None, None, None, 1, 4, 1, 64, ctypes.c_float(0.125), None, ctypes.c_size_t(0), None)
+    assert rc == -1
+    assert b"null" in lib.vc_last_error()
+    g = lib.vc_argmax
+    g.restype = ctypes.c_int
+    assert g(None, 1, 10, None, None) == -1
+    h = lib.vc_accept
+    h.restype = ctypes.c_int
+    assert h(None, None, 1, 2, 3, None, None, None) == -1
+
+
+def test_no_oracle_in_product_path():
+    """The product package never imports the oracle, and the oracle never imports the product."""
+    pkg = os.path.join(ROOT, "compressed_kv_draft_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".cpp", ".h")):
+                txt = open(os.path.join(dirpath, fn)).read()
+                assert not re.search(r"\boracle\b", txt.replace("no CPU fallback", "")) or fn.endswith(".md"), fn
+    for fn in os.listdir(os.path.join(ROOT, "oracle")):
+        if fn.endswith(".py"):
+            assert "compressed_kv_draft_amd" not in open(os.path.join(ROOT, "oracle", fn)).read(), fn

@@ -1,0 +1,254 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle on the same
+seeded inputs.  Sizes span several key tiles, several splits and ragged tails.
+
+Bars: bit-exact for codes, scales/zeros, dequantised values, token ids, accept
+lengths and copied bytes; relative L2 <= 1e-3 and max-abs <= 5e-3 * max|ref| for
+attention outputs.
+"""
+import numpy as np
+import pytest
+
+import oracle.vc_oracle as O
+from oracle import round as R
+from synth import configs as C
+from synth import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 1e-3
+MAX_ABS = 5e-3
+
+
+def _vc():
+    import compressed_kv_draft_amd as vc
+    return vc
+
+
+def assert_close(got, ref, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.isfinite(got).all(), what
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
+    mx = np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-300)
+    print(f"[parity] {what}: rel_l2={rel:.3e} max_abs/max|ref|={mx:.3e}", flush=True)
+    assert rel <= REL_L2 and mx <= MAX_ABS, (what, rel, mx)
+
+
+DRAFT_CASES = [
+    C.TINY,
+    C.TINY.with_(name="int2_d128_g4", B=2, Hq=8, Hkv=2, D=128, L=1056, k=5, bits=2, residual=32, seed=21),
+    C.TINY.with_(name="int4_d128_g8", B=1, Hq=16, Hkv=2, D=128, L=800, k=3, bits=4, residual=32, seed=22),
+    C.TINY.with_(name="int2_d64_g8_long", B=1, Hq=8, Hkv=1, D=64, L=4128, k=2, bits=2, residual=32, seed=23),
+    C.TINY.with_(name="identity_d128_g8", B=2, Hq=16, Hkv=2, D=128, L=777, k=3, kind="identity", seed=24),
+    C.TINY.with_(name="drop_d128_g8", B=2, Hq=16, Hkv=2, D=128, L=1000, k=4, kind="token_drop",
+                 keep_frac=0.1, seed=25),
+    C.TINY.with_(name="drop_d64_g4", B=1, Hq=4, Hkv=1, D=64, L=3000, k=2, kind="token_drop",
+                 keep_frac=0.3, seed=26),
+]
+
+
+@pytest.mark.parametrize("w", DRAFT_CASES, ids=lambda w: w.name)
+def test_draft_parity(w):
+    print(f"[case] draft {w.name}", flush=True)
+    from compressed_kv_draft_amd.workload import DeviceWorkload
+    dw = DeviceWorkload(w, with_vocab=False)
+    for j in range(w.k):
+        dw.draft_step(j)
+    got = dw.draft_out.cpu().numpy()       # [k, B, Hq, D]
+    g = w.g
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            keep = dw.keep_np[b, h] if w.kind == "token_drop" else None
+            ref = R.unit_draft(w, dw.np["K"][b, h], dw.np["V"][b, h], dw.np["Kn"][b, h], dw.np["Vn"][b, h],
+                               dw.np["Q"][b, h * g:(h + 1) * g], keep=keep)          # [g, k, D]
+            assert_close(got[:, b, h * g:(h + 1) * g].transpose(1, 0, 2), ref, f"{w.name} b{b} h{h}")
+
+
+QUANT_CASES = [(64, 4), (64, 2), (128, 4), (128, 2)]
+
+
+@pytest.mark.parametrize("D,bits", QUANT_CASES)
+def test_quantize_bit_exact(D, bits):
+    import torch
+    vc = _vc()
+    print(f"[case] quantize D={D} bits={bits}", flush=True)
+    w = C.TINY.with_(B=2, Hkv=2, Hq=4, D=D, L=320, seed=31 + D + bits)
+    K = I.context_kv(w, "k")
+    V = I.context_kv(w, "v")
+    # edge groups: a constant K group, a constant V group, a tiny-range group, a huge-range group
+    K[0, 0, 32:64, 3] = K[0, 0, 32, 3]
+    V[1, 1, 7, 0:32] = V[1, 1, 7, 0]
+    K[1, 0, 64:96, 5] = np.uint16(0x3F80) + np.arange(32, dtype=np.uint16) % 2   # 1.0 and 1.0078125
+    V[0, 1, 9, 32:64] = np.where(np.arange(32) % 2, np.uint16(0x4700), np.uint16(0xC700))  # +-32768
+    K[0, 1, 0:32, 0] = np.uint16(0x3A83) + np.arange(32, dtype=np.uint16) % 4   # scale is an f16 subnormal
+    nq = 288
+    from compressed_kv_draft_amd.workload import bf16_dev
+    kd, vd = bf16_dev(K, "cuda"), bf16_dev(V, "cuda")
+    comp = vc.quantize_kv(kd, vd, bits, nq)
+    torch.cuda.synchronize()
+    kc = comp.t["k_codes"].cpu().numpy()
+    vcd = comp.t["v_codes"].cpu().numpy()
+    km = comp.t["k_meta"].cpu().numpy()
+    vm = comp.t["v_meta"].cpu().numpy()
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            kf = O.bf16_to_f64(K[b, h, :nq]).astype(np.float32)
+            vf = O.bf16_to_f64(V[b, h, :nq]).astype(np.float32)
+            c, s, z = O.quantize_k(kf, bits)
+            assert np.array_equal(kc[b, h], O.pack_codes(c, bits)), (b, h, "k codes")
+            assert np.array_equal(km[b, h, ..., 0].view(np.uint16), s.view(np.uint16)), (b, h, "k scale")
+            assert np.array_equal(km[b, h, ..., 1].view(np.uint16), z.view(np.uint16)), (b, h, "k zero")
+            dq = vc.debug_dequant(comp, w.B, w.Hkv, D, b, h, 0).cpu().numpy()
+            assert np.array_equal(dq.astype(np.float64), O.dequant_k(c, s, z)), (b, h, "k dequant")
+            c, s, z = O.quantize_v(vf, bits)
+            assert np.array_equal(vcd[b, h], O.pack_codes(c, bits)), (b, h, "v codes")
+            assert np.array_equal(vm[b, h, ..., 0].view(np.uint16), s.view(np.uint16)), (b, h, "v scale")
+            assert np.array_equal(vm[b, h, ..., 1].view(np.uint16), z.view(np.uint16)), (b, h, "v zero")
+            dq = vc.debug_dequant(comp, w.B, w.Hkv, D, b, h, 1).cpu().numpy()
+            assert np.array_equal(dq.astype(np.float64), O.dequant_v(c, s, z)), (b, h, "v dequant")
+
+
+VERIFY_CASES = [
+    C.TINY,
+    C.TINY.with_(name="v_d128_g4_k32", B=2, Hq=8, Hkv=2, D=128, L=1000, k=32, seed=41),
+    C.TINY.with_(name="v_d128_g8_k32", B=1, Hq=16, Hkv=2, D=128, L=2085, k=32, seed=42),
+    C.TINY.with_(name="v_d64_g4_k3", B=3, Hq=8, Hkv=2, D=64, L=97, k=3, seed=43),
+    C.TINY.with_(name="v_paged_d128_g8", B=2, Hq=16, Hkv=2, D=128, L=1024, k=32, paged=True,
+                 page_tokens=16, seed=44),
+    C.TINY.with_(name="v_paged_d64_pt32", B=2, Hq=4, Hkv=1, D=64, L=320, k=7, paged=True,
+                 page_tokens=32, seed=45),
+]
+
+
+@pytest.mark.parametrize("w", VERIFY_CASES, ids=lambda w: w.name)
+def test_verify_parity(w):
+    from compressed_kv_draft_amd.workload import DeviceWorkload
+    print(f"[case] verify {w.name}", flush=True)
+    w = w.with_(kind="identity")
+    dw = DeviceWorkload(w, with_vocab=False)
+    got = dw.verify().cpu().numpy()      # [B, Hq, n_q, D]
+    g = w.g
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            ref = R.unit_verify(w, dw.np["K"][b, h], dw.np["V"][b, h], dw.np["Kn"][b, h], dw.np["Vn"][b, h],
+                                dw.np["Q"][b, h * g:(h + 1) * g])
+            assert_close(got[b, h * g:(h + 1) * g], ref, f"{w.name} b{b} h{h}")
+
+
+def test_verify_prefill_causal():
+    """ctx_len = 0 and many positions: plain causal self-attention (prefill)."""
+    import torch
+    vc = _vc()
+    from compressed_kv_draft_amd.workload import bf16_dev
+    print("[case] verify prefill", flush=True)
+    rng = np.random.default_rng(7)
+    B, Hq, Hkv, D, n = 1, 8, 2, 64, 300
+    q = (rng.standard_normal((B, Hq, n, D)) ).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, n, D)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, n, D)).astype(np.float32)
+    from synth.gen import f32_to_bf16_bits
+    qb, kb, vb = (f32_to_bf16_bits(x) for x in (q, k, v))
+    kd, vd = bf16_dev(kb, "cuda"), bf16_dev(vb, "cuda")
+    full = vc.FullKV(kd, vd, L_cap=n)
+    ctx = torch.zeros(B, dtype=torch.int32, device="cuda")
+    scale = O.scale_for(D)
+    got = vc.verify_attn(bf16_dev(qb, "cuda"), full, ctx, 0, Hkv, scale).cpu().numpy()
+    g = Hq // Hkv
+    for h in range(Hkv):
+        ref = O.verify_attention_unit(O.bf16_to_f64(qb[0, h * g:(h + 1) * g]), O.bf16_to_f64(kb[0, h]),
+                                      O.bf16_to_f64(vb[0, h]), 0, scale)
+        assert_close(got[0, h * g:(h + 1) * g], ref, f"prefill h{h}")
+
+
+def test_verify_future_rows_do_not_leak():
+    """Perturbing rows after L + j leaves verify position j bitwise unchanged."""
+    from compressed_kv_draft_amd.workload import DeviceWorkload
+    w = C.TINY.with_(name="leak", B=1, Hq=8, Hkv=2, D=128, L=500, k=6, kind="identity", seed=51)
+    dw = DeviceWorkload(w, with_vocab=False)
+    base = dw.verify().clone()
+    j = 2
+    dw.full_k[:, :, w.L + j + 1:] += 3.0
+    dw.full_v[:, :, w.L + j + 1:] -= 2.0
+    pert = dw.verify()
+    assert bool((pert[:, :, :j + 1] == base[:, :, :j + 1]).all())
+    assert not bool((pert[:, :, j + 1:] == base[:, :, j + 1:]).all())
+
+
+def test_accept_and_argmax():
+    import torch
+    vc = _vc()
+    print("[case] accept", flush=True)
+    rng = np.random.default_rng(9)
+    for (B, k, V) in [(4, 8, 1000), (3, 32, 32000), (2, 0, 77), (5, 5, 13)]:
+        logits = rng.standard_normal((B, k + 1, V)).astype(np.float32)
+        y = np.array([[O.argmax_first(logits[b, j]) for j in range(k + 1)] for b in range(B)])
+        d = y[:, :k].copy()
+        for b in range(B):
+            if k and b % 2 == 1:
+                i = int(rng.integers(0, k))
+                d[b, i] = (d[b, i] + 1) % V
+        lt = torch.from_numpy(logits).cuda()
+        dt = torch.from_numpy(d.astype(np.int32)).cuda()
+        out, n = vc.accept(dt, lt)
+        out, n = out.cpu().numpy(), n.cpu().numpy()
+        for b in range(B):
+            ro, rn = O.accept(d[b], y[b])
+            assert n[b] == rn and list(out[b]) == list(ro), (B, k, V, b)
+    # ties -> lowest index, V not a multiple of 4
+    x = np.zeros((3, 10), np.float32)
+    x[0, [3, 7]] = 5.0
+    x[1, :] = -1.0
+    x[2, 9] = 1.0
+    ids = vc.argmax(torch.from_numpy(x).cuda()).cpu().numpy()
+    assert list(ids) == [3, 0, 9]
+
+
+def test_round_tiny_tokens_bit_exact():
+    """Single-layer round at the tiny workload: query vectors are resampled until
+    every top-1 margin exceeds the bound, then draft tokens, verify tokens,
+    emitted ids and the accept length must equal the oracle's."""
+    import torch
+    vc = _vc()
+    from compressed_kv_draft_amd.workload import DeviceWorkload
+    for w in (C.TINY, C.TINY.with_(kind="identity", name="tiny_identity")):
+        print(f"[case] round {w.name}", flush=True)
+        K, V = I.context_kv(w, "k"), I.context_kv(w, "v")
+        Kn, Vn = I.new_rows(w, "k"), I.new_rows(w, "v")
+        W = I.vocab_matrix(w)
+        attempts, Qb, r = R.plant_margins(w, 0, K[0], V[0], Kn[0], Vn[0], W)
+        dw = DeviceWorkload(w, Q=Qb[None])
+        for j in range(w.k):
+            dw.draft_step(j)
+        d_ids = vc.argmax(dw.draft_logits().contiguous()).reshape(w.B, w.k)
+        dw.verify()
+        out, n = vc.accept(d_ids, dw.verify_logits())
+        torch.cuda.synchronize()
+        assert list(d_ids.cpu().numpy()[0]) == list(r["draft_ids"])
+        assert int(n.cpu().numpy()[0]) == r["n_accept"]
+        assert list(out.cpu().numpy()[0]) == list(r["out_ids"])
+        if w.kind == "identity":
+            assert r["n_accept"] == w.k
+
+
+def test_prefetch_pages_bit_exact():
+    import torch
+    vc = _vc()
+    print("[case] prefetch", flush=True)
+    page_bytes, slots, nseq, pps, pt = 4096, 64, 4, 16, 16
+    rng = np.random.default_rng(3)
+    table = rng.permutation(slots).astype(np.int32).reshape(nseq, pps)
+    host = torch.empty(slots * page_bytes, dtype=torch.uint8, pin_memory=True)
+    host.copy_(torch.from_numpy(rng.integers(0, 256, slots * page_bytes, dtype=np.uint8)))
+    dev0 = rng.integers(0, 256, slots * page_bytes, dtype=np.uint8)
+    dev = torch.from_numpy(dev0).cuda()
+    s = torch.cuda.Stream()
+    vc.prefetch_full_kv(host, dev, page_bytes, table, [1, 3], 40, 200, pt, stream=s)
+    s.synchronize()
+    want = O.prefetch_expected(dev0.reshape(slots, page_bytes), host.numpy().reshape(slots, page_bytes),
+                               table, [1, 3], 40, 200, pt)
+    assert np.array_equal(dev.cpu().numpy().reshape(slots, page_bytes), want)
+    # unpinned host memory is rejected before anything is enqueued
+    with pytest.raises(vc.VcError):
+        vc.prefetch_full_kv(torch.empty(slots * page_bytes, dtype=torch.uint8), dev, page_bytes, table, [0],
+                            0, 16, pt, stream=s)
