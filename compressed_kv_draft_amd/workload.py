@@ -133,3 +133,49 @@ class DeviceWorkload:
         w = self.w
         o = self.verify_out.permute(0, 2, 1, 3).reshape(w.B, w.n_q, w.Hq * w.D)
         return torch.matmul(o, self.W).contiguous()
+
+
+def clone_compressed(comp: vc.Compressed) -> vc.Compressed:
+    """Same cache contents in fresh device buffers (another 'layer' for rotation)."""
+    t = dict(comp.t)
+    for f in ("k_codes", "v_codes", "k_meta", "v_meta", "keep_idx"):
+        if t.get(f) is not None:
+            t[f] = t[f].clone()
+    for f in ("k_full", "v_full"):
+        if t.get(f) is not None:
+            t[f] = t[f].clone()
+    t.pop("src_keepalive", None)
+    return vc.Compressed(comp.kind, **t)
+
+
+def draft_step_bytes(w: Workload, j: int) -> int:
+    """Algorithmic HBM bytes of draft step j: everything the method must read
+    (compressed codes + scales/zeros, or gathered rows + indices, plus the exact
+    tail rows and the queries) and write (outputs)."""
+    units = w.B * w.Hkv
+    D = w.D
+    if w.kind == "quant":
+        nq = w.n_quant
+        per = 2 * nq * D * w.bits // 8 + (nq // 32) * D * 4 + nq * (D // 32) * 4
+        tail = w.residual + j + 1
+    elif w.kind == "token_drop":
+        per = w.n_keep * (2 * D * 2 + 4)
+        tail = j + 1
+    else:
+        per = w.L * 2 * D * 2
+        tail = j + 1
+    per += tail * 2 * D * 2
+    return units * per + w.B * w.Hq * D * (2 + 4)
+
+
+def verify_bytes(w: Workload) -> int:
+    """Algorithmic HBM bytes of one verify: the full K/V rows [0, L + n_q) once,
+    the queries and the fp32 outputs."""
+    n = w.L + w.n_q
+    return w.B * w.Hkv * n * 2 * w.D * 2 + w.B * w.Hq * w.n_q * w.D * (2 + 4)
+
+
+def verify_flops(w: Workload) -> int:
+    """q.k and p.v MACs x 2 over the causal key ranges."""
+    keys = sum(w.L + j + 1 for j in range(w.n_q))
+    return 2 * 2 * w.B * w.Hq * keys * w.D
