@@ -3,29 +3,44 @@
 // [VC Core Algorithm: drafting generates candidate tokens with KV_comp;
 //  VC Key System Innovations P1: drafting is GPU-HBM-bandwidth bound]
 //
-// Vector-ALU kernel.  A workgroup (4 wavefronts) owns one (batch, kv-head)
-// and one split of its keys.  Inside a wavefront, 8 lanes share a key: each
-// holds D/8 channels, dequantises them in registers (fp32, a single fma per
-// value), forms partial q.k dot products for the g query heads of the GQA
-// group and reduces them with 3 lane shuffles.  Every 8-lane slot keeps its own
-// online-softmax state (running max in log2 units, sum, unnormalised output for
-// its channels); slots are merged with lane shuffles and the 4 wavefronts in
-// LDS at the end.  Splits are merged by draft_combine_kernel.
+// The g query heads of a GQA group read the same compressed K/V, so q.K^T and
+// P.V are thin matrix products (g rows).  With int2/int4 codes they carry 20-26
+// multiply-adds per HBM byte, more than fp32 vector ALUs sustain at HBM speed,
+// so both products run on the f16 matrix cores, exactly:
+//  * a code c placed in the mantissa of an f16 bit pattern is the subnormal
+//    c * 2^(bits*jj - 24) (jj = its position in the byte) -- one AND turns two
+//    packed codes into two exact f16 operands;
+//  * K is grouped per channel, so its scale goes into the query: q_h * s is
+//    computed in f16 as hi + lo (a rounded product and its exact residual, one
+//    fma), giving 22 significand bits; hi and lo are adjacent MFMA columns;
+//  * V is grouped per token and channel group G, so its scale goes into the
+//    probabilities: p * s_{t,G} is split into f16 hi and lo and applied in two
+//    products; the zero points enter as sum_t p_t z_{t,G} (fp32) and, for K,
+//    as one more small product z . q per 32-token group.
+// Exact bf16 rows (the uncompressed recent window and this round's drafted
+// rows, or the identity / token-dropped caches) use bf16 products: q.k exactly,
+// P.V with P split into bf16 hi + lo, V transposed through LDS with the gfx950
+// transpose read.
+//
+// Work split: a workgroup (4 wavefronts) owns one (batch, kv-head) and a range
+// of 32-token blocks; wavefronts take every 4th block and keep their own
+// online-softmax state, merged in LDS at the end.  Workgroups past the main
+// splits handle the exact tail.  draft_combine_kernel merges the splits.
+#include "mfma.h"
 #include "vc_common.h"
 
 namespace vc {
 namespace {
 
-struct alignas(4) H2 {
-  _Float16 s, z;
-};
-
 struct DraftArgs {
-  int kind, bits, n_quant, L_full, L_cap, n_keep;
+  int n_main;    // rows of the compressed part (quant: n_quant; identity: L_full; drop: n_keep)
+  int n_quant;
+  int L_cap;
+  int row_bound;  // valid physical rows of k_full/v_full (identity / drop)
   const uint8_t* k_codes;
   const uint8_t* v_codes;
-  const H2* k_meta;
-  const H2* v_meta;
+  const uint32_t* k_meta;  // f16x2 {scale, zero}
+  const uint32_t* v_meta;
   const uint16_t* k_full;
   const uint16_t* v_full;
   const int32_t* keep_idx;
@@ -38,201 +53,495 @@ struct DraftArgs {
   float* lse;
   int B, Hq, Hkv, g;
   float scale_log2;
-  int n_main;
-  int keys_per_split;
-  int splits;
+  int main_splits, main_bpw;  // workgroups for the compressed part, blocks per workgroup
+  int tail_bpw;               // blocks per tail workgroup
+  int splits;                 // all workgroups of one (batch, kv-head)
   float* ws;
 };
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+constexpr float kTau = 8.0f;  // lazy rescale: the running max moves only when exceeded by 2^8
+constexpr int kQExp = 4;      // q is scaled by 2^kQExp before it multiplies the K scales
 
-// Load CPL consecutive bf16 values as fp32.
-template <int CPL>
-__device__ __forceinline__ void load_bf16_row(const uint16_t* p, float* x) {
-  static_assert(CPL % 8 == 0, "");
-#pragma unroll
-  for (int c = 0; c < CPL; c += 8) {
-    const uint4 w = *reinterpret_cast<const uint4*>(p + c);
-    x[c + 0] = bf16_lo(w.x);
-    x[c + 1] = bf16_hi(w.x);
-    x[c + 2] = bf16_lo(w.y);
-    x[c + 3] = bf16_hi(w.y);
-    x[c + 4] = bf16_lo(w.z);
-    x[c + 5] = bf16_hi(w.z);
-    x[c + 6] = bf16_lo(w.w);
-    x[c + 7] = bf16_hi(w.w);
-  }
+template <int D, int BITS>
+struct Cfg {
+  static constexpr int NKS = D / 32;   // k-steps of q.k
+  static constexpr int NCT = D / 16;   // 16-channel column tiles of P.V
+  static constexpr int NG = D / 32;    // V channel groups
+  static constexpr int B_ = BITS > 0 ? BITS : 2;
+  static constexpr int CPD = 32 / B_;  // K channels per code dword
+  static constexpr int PPD = CPD / 2;  // code pairs per dword
+  static constexpr int PER = 8 / B_;   // codes per byte
+  static constexpr uint32_t MASK = B_ == 2 ? 0x00030003u : 0x000F000Fu;
+  static constexpr int KDW = D * B_ / 128;  // K code dwords per lane per 16-token tile
+  static constexpr int VDW = D * B_ / 64;   // V code dwords per lane per block
+  static constexpr int VMD = NG / 2;        // V meta dwords staged per lane per block
+  static constexpr int VPITCH = D + 16;     // LDS row pitch (elements) of staged bf16 V
+  static constexpr int META_DW = BITS > 0 ? 2 * 16 * NKS + 32 * NG : 0;
+  static constexpr int STAGE_BYTES = META_DW * 4 + 32 * VPITCH * 2;
+  static constexpr int EPI_BYTES = kWaves * (8 * D + 8 + 8 + 8 * 4) * 4;
+  static constexpr int SMEM = kWaves * STAGE_BYTES > EPI_BYTES ? kWaves * STAGE_BYTES : EPI_BYTES;
+};
+
+// Two packed codes (bits b and b+16 of w, position j of the dword) as an f16 pair:
+// code * 2^(bits * (j % PER) - 24) each, exactly.
+template <int BITS>
+__device__ __forceinline__ uint32_t code_pair(uint32_t w, int j) {
+  constexpr int PER = 8 / BITS;
+  constexpr uint32_t MASK = BITS == 2 ? 0x00030003u : 0x000F000Fu;
+  return (w >> (8 * (j / PER))) & (MASK << (BITS * (j % PER)));
 }
 
-// Unpack CPL codes (canonical packing) starting at channel c0 of a code row.
-template <int CPL, int BITS>
-__device__ __forceinline__ void load_codes(const uint8_t* row, int c0, uint32_t* code) {
-  constexpr int BYTES = CPL * BITS / 8;
-  const uint8_t* p = row + c0 * BITS / 8;
-  uint64_t w;
-  if constexpr (BYTES == 8) {
-    w = *reinterpret_cast<const uint64_t*>(p);
-  } else if constexpr (BYTES == 4) {
-    w = *reinterpret_cast<const uint32_t*>(p);
+// N consecutive dwords from an address aligned to min(16, 4N) bytes.
+template <int N>
+__device__ __forceinline__ void load_dwords(const void* p, uint32_t* out) {
+  if constexpr (N == 1) {
+    out[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else if constexpr (N == 2) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    out[0] = w.x;
+    out[1] = w.y;
   } else {
-    w = *reinterpret_cast<const uint16_t*>(p);
-  }
+    static_assert(N % 4 == 0, "");
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) code[c] = (uint32_t)(w >> (BITS * c)) & ((1u << BITS) - 1u);
-}
-
-// Fetch the CPL channels [c0, c0 + CPL) of key `key` of unit `unit` as fp32.
-template <int D, int CPL, int BITS>
-__device__ __forceinline__ void fetch_key_row(const DraftArgs& a, int unit, int b, int key, int c0,
-                                              bool is_k, float* x) {
-  if (key < a.n_main) {
-    if (BITS > 0) {  // QUANT
-      constexpr int RB = D * BITS / 8;
-      const uint8_t* codes = (is_k ? a.k_codes : a.v_codes) + ((size_t)unit * a.n_quant + key) * RB;
-      uint32_t code[CPL];
-      load_codes<CPL, BITS>(codes, c0, code);
-      if (is_k) {
-        const H2* m = a.k_meta + ((size_t)unit * (a.n_quant / 32) + key / 32) * D + c0;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          const H2 sz = m[c];
-          x[c] = fmaf((float)code[c], (float)sz.s, (float)sz.z);
-        }
-      } else {
-        const H2 sz = a.v_meta[((size_t)unit * a.n_quant + key) * (D / 32) + c0 / 32];
-        const float s = (float)sz.s, z = (float)sz.z;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) x[c] = fmaf((float)code[c], s, z);
-      }
-    } else {
-      int row = key;
-      if (a.kind == VC_KV_TOKEN_DROP) row = a.keep_idx[(size_t)unit * a.n_keep + key];
-      const uint16_t* src = is_k ? a.k_full : a.v_full;
-      if (row < 0 || row >= a.L_cap) {  // invalid index: contributes nothing
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) x[c] = 0.0f;
-        return;
-      }
-      load_bf16_row<CPL>(src + ((size_t)unit * a.L_cap + row) * D + c0, x);
+    for (int k = 0; k < N / 4; ++k) {
+      const u32x4 w = reinterpret_cast<const u32x4*>(p)[k];
+      out[4 * k] = w[0];
+      out[4 * k + 1] = w[1];
+      out[4 * k + 2] = w[2];
+      out[4 * k + 3] = w[3];
     }
-  } else {
-    const uint16_t* src = is_k ? a.tail_k : a.tail_v;
-    load_bf16_row<CPL>(src + ((size_t)unit * a.T_cap + (key - a.n_main)) * D + c0, x);
   }
 }
 
-template <int D, int GM, int BITS>
-__global__ __launch_bounds__(kThreads) void draft_valu_kernel(DraftArgs a) {
-  constexpr int CPL = D / 8;
+__device__ __forceinline__ float f16lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[0]; }
+__device__ __forceinline__ float f16hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[1]; }
+
+// Per-lane softmax state: running max m (log2 units) of this lane's head, the
+// partial sum l over this lane's tokens, zero-point sums, output accumulators.
+template <int NCT, int NV>
+struct State {
+  float m, l;
+  float zacc[NV];
+  f32x4 O[NCT];
+};
+
+// Online softmax over the 8 scores a lane holds for one block (its head, tokens
+// 4q..4q+3 and 16+4q..16+4q+3).  The running max only moves when a score exceeds
+// it by kTau, so the accumulators are rescaled rarely; P <= 2^kTau.
+template <int NCT, int NV>
+__device__ __forceinline__ void softmax_block(const float (&x)[8], State<NCT, NV>& st, float (&P)[8], int quad) {
+  float tmax = x[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, x[e]);
+  tmax = fmaxf(tmax, shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+  const bool need = tmax > st.m + kTau;
+  if (__any(need)) {
+    const float mn = fmaxf(st.m, tmax);
+    const float alpha = mn == kNegInf ? 1.0f : fast_exp2(st.m - mn);
+    st.l *= alpha;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) st.zacc[v] *= alpha;
+    // output row 4q+i belongs to the head of column 4q+i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ar = __shfl(alpha, 4 * quad + i, 64);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) st.O[ct][i] *= ar;
+    }
+    st.m = mn;
+  }
+  const float mu = st.m == kNegInf ? 0.0f : st.m;
+  float ps = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    P[e] = fast_exp2(x[e] - mu);
+    ps += P[e];
+  }
+  st.l += ps;
+}
+
+// Source of exact bf16 rows: the tail, the identity cache or the kept rows.
+struct RowSrc {
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* idx;  // logical -> physical row (token drop) or nullptr
+  size_t unit_row0;    // first row of this (batch, kv-head)
+  int n_valid;         // logical rows
+  int bound;           // physical rows in [0, bound) are readable
+};
+
+// One block of 32 exact rows: q.k on bf16 matrix cores, P.V with P = hi + lo in
+// bf16 and V staged in LDS, read transposed.
+template <int D, int NV>
+__device__ __forceinline__ void rows_block(const RowSrc& src, int blk, const bf16x8 (&qb)[D / 32], float scale_log2,
+                                           uint16_t* vst, State<D / 16, NV>& st, int lane, int col, int quad,
+                                           int hilo) {
+  constexpr int NKS = D / 32, NCT = D / 16, VPITCH = D + 16;
+  const int t0 = blk * 32;
+  // physical row of logical row t0 + (lane & 31), or -1
+  int myrow = -1;
+  {
+    const int t = t0 + (lane & 31);
+    if (t < src.n_valid) {
+      const int p = src.idx != nullptr ? src.idx[t] : t;
+      myrow = (p >= 0 && p < src.bound) ? p : -1;
+    }
+  }
+  // K rows of tokens col and 16 + col, this quad's D/4 channels
+  u32x4 kr[2][NKS];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int pr = __shfl(myrow, 16 * tt + col, 64);
+    const uint16_t* p = src.k + (src.unit_row0 + (size_t)(pr < 0 ? 0 : pr)) * D + quad * (D / 4);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      kr[tt][ks] = pr >= 0 ? *reinterpret_cast<const u32x4*>(p + 8 * ks) : u32x4{0u, 0u, 0u, 0u};
+  }
+  // V rows into LDS (row-major, padded pitch)
+#pragma unroll
+  for (int u = 0; u < D / 16; ++u) {
+    const int c = lane + 64 * u;
+    const int row = c / (D / 8), off = (c % (D / 8)) * 8;
+    const int pr = __shfl(myrow, row, 64);
+    const u32x4 val = pr >= 0 ? *reinterpret_cast<const u32x4*>(src.v + (src.unit_row0 + (size_t)pr) * D + off)
+                              : u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(vst + row * VPITCH + off) = val;
+  }
+  // scores (log2 units), invalid rows masked
+  float x[8];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) acc = mfma_bf16(__builtin_bit_cast(bf16x8, kr[tt][ks]), qb[ks], acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * tt + 4 * quad + i;
+      const int pr = __shfl(myrow, r, 64);
+      x[4 * tt + i] = pr >= 0 ? acc[i] * scale_log2 : kNegInf;
+    }
+  }
+  float P[8];
+  softmax_block<NCT, NV>(x, st, P, quad);
+  // A operand: bf16 hi part (even columns) or lo residual (odd columns) of P
+  u32x4 ap;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float p = P[2 * k + h];
+      const uint32_t hb = __float_as_uint(p) & 0xFFFF0000u;
+      const float lo = p - __uint_as_float(hb);
+      w[h] = (hilo ? __float_as_uint(lo) : hb) >> 16;
+    }
+    ap[k] = w[0] | (w[1] << 16);
+  }
+  const bf16x8 A = __builtin_bit_cast(bf16x8, ap);
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const uint16_t* base = vst + 16 * ct + 4 * (col & 3);
+    const s16x4 lo4 = lds_read_tr16(base + (4 * quad + (col >> 2)) * VPITCH);
+    const s16x4 hi4 = lds_read_tr16(base + (16 + 4 * quad + (col >> 2)) * VPITCH);
+    const s16x8 bv8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+    st.O[ct] = mfma_bf16(A, __builtin_bit_cast(bf16x8, bv8), st.O[ct]);
+  }
+}
+
+template <int D, int BITS, int NV>
+__global__ __launch_bounds__(kThreads) void draft_mfma_kernel(DraftArgs a) {
+  using C = Cfg<D, BITS>;
+  constexpr int NKS = C::NKS, NCT = C::NCT, NG = C::NG;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM];
+
   const int unit = blockIdx.y;
-  const int b = unit / a.Hkv;
-  const int hk = unit % a.Hkv;
+  const int b = unit / a.Hkv, hk = unit % a.Hkv;
   const int split = blockIdx.x;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int slot = lane >> 3;
-  const int c0 = (lane & 7) * CPL;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, quad = lane >> 4;
   const int g = a.g;
+  // column / row r of the 16-wide tiles <-> (head, hi-or-lo, replica)
+  const int hp = col >> 1, hilo = col & 1;
+  const int head = hp % g, rep = hp / g;
+  const int R8 = 8 / g, SP = 2 * R8;  // replicas of the head set; V-group slots per head
+  const int slot = 2 * rep + hilo;
+  const bool slot_ok = rep < R8;
 
-  int tl = a.T_cap > 0 ? a.tail_len[b] : 0;
-  tl = tl < 0 ? 0 : (tl > a.T_cap ? a.T_cap : tl);
-  const int n_keys = a.n_main + tl;
-  const int k0 = split * a.keys_per_split;
-  int k1 = k0 + a.keys_per_split;
-  k1 = k1 < n_keys ? k1 : n_keys;
+  unsigned char* stage = smem + wave * C::STAGE_BYTES;
+  uint32_t* sp = reinterpret_cast<uint32_t*>(stage);  // [4 quads][NKS][4] K-scale pairs
+  uint32_t* zp = sp + 16 * NKS;                       // [4][NKS][4] K-zero pairs
+  uint32_t* vm = zp + 16 * NKS;                       // [NG][4 quads][8 slots] V {scale, zero}
+  uint16_t* vst = reinterpret_cast<uint16_t*>(stage + C::META_DW * 4);
 
-  float qf[GM][CPL];
+  // this lane's query head, channels quad * D/4 .. + D/4
+  const uint16_t* qrow = a.q + ((size_t)b * a.Hq + hk * g + head) * D + quad * (D / 4);
+  u32x4 qraw[NKS];
 #pragma unroll
-  for (int h = 0; h < GM; ++h) {
-    if (h < g) {
-      load_bf16_row<CPL>(a.q + ((size_t)b * a.Hq + hk * g + h) * D + c0, qf[h]);
-    } else {
+  for (int ks = 0; ks < NKS; ++ks) qraw[ks] = *reinterpret_cast<const u32x4*>(qrow + 8 * ks);
+  bf16x8 qb[NKS];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) qf[h][c] = 0.0f;
-    }
-  }
-  float m[GM], l[GM], o[GM][CPL];
-#pragma unroll
-  for (int h = 0; h < GM; ++h) {
-    m[h] = kNegInf;
-    l[h] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) o[h][c] = 0.0f;
-  }
+  for (int ks = 0; ks < NKS; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, qraw[ks]);
 
-  const int span = k1 > k0 ? k1 - k0 : 0;
-  const int iters = (span + 8 * kWaves - 1) / (8 * kWaves);
-  for (int it = 0; it < iters; ++it) {
-    const int key = k0 + (it * kWaves + wave) * 8 + slot;
-    const bool valid = key < k1;
-    float kx[CPL];
-    if (valid) {
-      fetch_key_row<D, CPL, BITS>(a, unit, b, key, c0, true, kx);
-    } else {
+  State<NCT, NV> st;
+  st.m = kNegInf;
+  st.l = 0.0f;
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) kx[c] = 0.0f;
-    }
-    float s[GM];
+  for (int v = 0; v < NV; ++v) st.zacc[v] = 0.0f;
 #pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      float acc = 0.0f;
+  for (int ct = 0; ct < NCT; ++ct) st.O[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const bool is_tail = split >= a.main_splits;
+  const size_t unit_rows = (size_t)unit;
+
+  if (!is_tail) {
+    const int nb = (a.n_main + 31) / 32;
+    const int blo = split * a.main_bpw;
+    const int bhi = min(blo + a.main_bpw, nb);
+    if constexpr (BITS > 0) {
+      // ---------------------------------------------------------------- quant
+      // q scaled per k slot (f16, exact): qF = q 2^(kQExp - bits*jj); qz = q
+      uint32_t qF[NKS][4], qz[NKS][4];
+      {
+        const uint16_t* qh = reinterpret_cast<const uint16_t*>(qraw);
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) acc = fmaf(qf[h][c], kx[c], acc);
-      acc += shfl_xor(acc, 1);
-      acc += shfl_xor(acc, 2);
-      acc += shfl_xor(acc, 4);
-      s[h] = acc * a.scale_log2;
-    }
-    if (valid) {
-      float vx[CPL];
-      fetch_key_row<D, CPL, BITS>(a, unit, b, key, c0, false, vx);
+        for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
-      for (int h = 0; h < GM; ++h) {
-        if (h < g) {
-          const float mn = fmaxf(m[h], s[h]);
-          const float alpha = fast_exp2(m[h] - mn);  // 0 when m was -inf
-          const float p = fast_exp2(s[h] - mn);
-          l[h] = fmaf(l[h], alpha, p);
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) o[h][c] = fmaf(o[h][c], alpha, p * vx[c]);
-          m[h] = mn;
+          for (int i = 0; i < 4; ++i) {
+            const int pi = 4 * ks + i, d = pi / C::PPD, j = pi % C::PPD;
+            const int ca = C::CPD * d + j, cb = ca + C::CPD / 2;
+            const float xa = bf16_to_f32(qh[ca]), xb = bf16_to_f32(qh[cb]);
+            const float f = __builtin_ldexpf(1.0f, kQExp - BITS * (j % C::PER));
+            const f16x2 pf = {(_Float16)(xa * f), (_Float16)(xb * f)};
+            const f16x2 pz = {(_Float16)xa, (_Float16)xb};
+            qF[ks][i] = __builtin_bit_cast(uint32_t, pf);
+            qz[ks][i] = __builtin_bit_cast(uint32_t, pz);
+          }
         }
       }
-    }
-  }
-
-  // merge the 8 slots of the wavefront (lanes with equal channel chunk)
-#pragma unroll
-  for (int mask = 8; mask < 64; mask <<= 1) {
-#pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      const float mo = shfl_xor(m[h], mask);
-      const float lo = shfl_xor(l[h], mask);
-      const float mn = fmaxf(m[h], mo);
-      const float wa = m[h] == kNegInf ? 0.0f : fast_exp2(m[h] - mn);
-      const float wb = mo == kNegInf ? 0.0f : fast_exp2(mo - mn);
-      l[h] = l[h] * wa + lo * wb;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const float oo = shfl_xor(o[h][c], mask);
-        o[h][c] = o[h][c] * wa + oo * wb;
+      const uint32_t lomask = hilo ? 0xFFFFFFFFu : 0u;
+      // K-meta pair this lane stages: (quad', ks', i') = lane
+      const int nq32 = a.n_quant / 32;
+      int kma = 0, kmb = 0;
+      const bool kstage = lane < 16 * NKS;
+      {
+        const int q_ = lane / (4 * NKS), ks_ = (lane / 4) % NKS, i_ = lane % 4;
+        const int pi = 4 * ks_ + i_, d = pi / C::PPD, j = pi % C::PPD;
+        kma = q_ * (D / 4) + C::CPD * d + j;
+        kmb = kma + C::CPD / 2;
       }
-      m[h] = mn;
+      const uint8_t* kcodes = a.k_codes + unit_rows * a.n_quant * (D * BITS / 8) + quad * (D * BITS / 32);
+      const uint8_t* vcodes = a.v_codes + unit_rows * a.n_quant * (D * BITS / 8) + lane * (C::VDW * 4);
+      const uint32_t* kmeta = a.k_meta + unit_rows * nq32 * D;
+      const uint32_t* vmeta = a.v_meta + unit_rows * a.n_quant * NG + lane * C::VMD;
+
+      struct Raw {
+        uint32_t kc[2][C::KDW];
+        uint32_t vc[C::VDW];
+        uint32_t km[2];
+        uint32_t vmt[C::VMD];
+      };
+      auto load = [&](int blk, Raw& r) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const uint8_t* p = kcodes + (size_t)(32 * blk + 16 * tt + col) * (D * BITS / 8);
+          load_dwords<C::KDW>(p, r.kc[tt]);
+        }
+        load_dwords<C::VDW>(vcodes + (size_t)blk * 64 * (C::VDW * 4), r.vc);
+        if (kstage) {
+          r.km[0] = kmeta[(size_t)blk * D + kma];
+          r.km[1] = kmeta[(size_t)blk * D + kmb];
+        } else {
+          r.km[0] = r.km[1] = 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < C::VMD; ++u) r.vmt[u] = vmeta[(size_t)blk * 32 * NG + u];
+      };
+
+      int blk = blo + wave;
+      Raw cur;
+      if (blk < bhi) load(blk, cur);
+      while (blk < bhi) {
+        // stage this block's meta in LDS (wavefront-private region; LDS ops of one
+        // wavefront complete in order, so the reads below see these writes)
+        if (kstage) {
+          sp[lane] = (cur.km[0] & 0xFFFFu) | (cur.km[1] << 16);
+          zp[lane] = (cur.km[0] >> 16) | (cur.km[1] & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int u = 0; u < C::VMD; ++u) {
+          const int d = lane * C::VMD + u, t = d / NG, G = d % NG;
+          vm[(G * 4 + (t % 16) / 4) * 8 + (t % 4) + 4 * (t / 16)] = cur.vmt[u];
+        }
+        const int nxt = blk + kWaves;
+        Raw nx;
+        if (nxt < bhi) load(nxt, nx);
+
+        // q~ = hi or lo part of qF * s_K, and the K zero-point product z . q
+        f32x4 accZ = {0.f, 0.f, 0.f, 0.f};
+        f16x8 qt[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const u32x4 z4 = *reinterpret_cast<const u32x4*>(zp + (quad * NKS + ks) * 4);
+          const u32x4 qz4 = {qz[ks][0], qz[ks][1], qz[ks][2], qz[ks][3]};
+          accZ = mfma_f16(__builtin_bit_cast(f16x8, z4), __builtin_bit_cast(f16x8, qz4), accZ);
+          const u32x4 s4 = *reinterpret_cast<const u32x4*>(sp + (quad * NKS + ks) * 4);
+          u32x4 r4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // (bit-casting the subscript s4[i] directly reads element 0: copy it out first)
+            const uint32_t sw = s4[i];
+            const f16x2 s = __builtin_bit_cast(f16x2, sw);
+            const f16x2 qf = __builtin_bit_cast(f16x2, qF[ks][i]);
+            const f16x2 hi = qf * s;
+            const f16x2 t = __builtin_bit_cast(f16x2, __builtin_bit_cast(uint32_t, hi) & lomask);
+            r4[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qf, s, -t));
+          }
+          qt[ks] = __builtin_bit_cast(f16x8, r4);
+        }
+        // code part of q.k for tokens col and 16 + col; hi + lo columns summed
+        float x[8];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            u32x4 a4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int pi = 4 * ks + i;
+              a4[i] = code_pair<BITS>(cur.kc[tt][pi / C::PPD], pi % C::PPD);
+            }
+            acc = mfma_f16(__builtin_bit_cast(f16x8, a4), qt[ks], acc);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float v = acc[i];
+            v += shfl_xor(v, 1);
+            x[4 * tt + i] = (v * 0x1p20f + accZ[i]) * a.scale_log2;
+          }
+        }
+        float P[8];
+        softmax_block<NCT, NV>(x, st, P, quad);
+        // A operands: hi and lo of P * s_V for this lane's channel group(s)
+        f16x8 Ahi[NV], Alo[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          const int G = slot + v * SP;
+          const bool gok = slot_ok && G < NG;
+          const int Gc = gok ? G : 0;
+          const u32x4 m0 = *reinterpret_cast<const u32x4*>(vm + (Gc * 4 + quad) * 8);
+          const u32x4 m1 = *reinterpret_cast<const u32x4*>(vm + (Gc * 4 + quad) * 8 + 4);
+          const uint32_t mm[8] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
+          float zs = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float s = f16lo(mm[e]), z = f16hi(mm[e]);
+            const float xs = P[e] * s;
+            zs = fmaf(P[e], z, zs);
+            const _Float16 h = (_Float16)xs;
+            Ahi[v][e] = gok ? h : (_Float16)0.0f;
+            Alo[v][e] = gok ? (_Float16)(xs - (float)h) : (_Float16)0.0f;
+          }
+          st.zacc[v] += gok ? zs : 0.0f;
+        }
+        // P.V code part
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          const int v = NV == 1 ? 0 : ct / 4;
+          u32x4 b4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int pi = i * NCT + ct;
+            b4[i] = code_pair<BITS>(cur.vc[pi / C::PPD], pi % C::PPD);
+          }
+          st.O[ct] = mfma_f16(Ahi[v], __builtin_bit_cast(f16x8, b4), st.O[ct]);
+          st.O[ct] = mfma_f16(Alo[v], __builtin_bit_cast(f16x8, b4), st.O[ct]);
+        }
+        cur = nx;
+        blk = nxt;
+      }
+    } else {
+      // ---------------------------------------------------- exact rows (main)
+      RowSrc src;
+      src.k = a.k_full;
+      src.v = a.v_full;
+      src.idx = a.keep_idx != nullptr ? a.keep_idx + unit_rows * a.n_main : nullptr;
+      src.unit_row0 = unit_rows * a.L_cap;
+      src.n_valid = a.n_main;
+      src.bound = a.row_bound;
+      for (int blk = blo + wave; blk < bhi; blk += kWaves)
+        rows_block<D, NV>(src, blk, qb, a.scale_log2, vst, st, lane, col, quad, hilo);
     }
+  } else {
+    // -------------------------------------------------------------- exact tail
+    int tl = a.T_cap > 0 ? a.tail_len[b] : 0;
+    tl = tl < 0 ? 0 : (tl > a.T_cap ? a.T_cap : tl);
+    RowSrc src;
+    src.k = a.tail_k;
+    src.v = a.tail_v;
+    src.idx = nullptr;
+    src.unit_row0 = unit_rows * a.T_cap;
+    src.n_valid = tl;
+    src.bound = a.T_cap;
+    const int nb = (tl + 31) / 32;
+    const int blo = (split - a.main_splits) * a.tail_bpw;
+    const int bhi = min(blo + a.tail_bpw, nb);
+    for (int blk = blo + wave; blk < bhi; blk += kWaves)
+      rows_block<D, NV>(src, blk, qb, a.scale_log2, vst, st, lane, col, quad, hilo);
   }
 
-  // merge the wavefronts in LDS
-  __shared__ float s_o[kWaves][GM][D];
-  __shared__ float s_ml[kWaves][GM][2];
-  if (slot == 0) {
+  // ------------------------------------------------------------------ epilogue
+  float lt = st.l;
+  lt += shfl_xor(lt, 16);
+  lt += shfl_xor(lt, 32);
+  float zt[NV];
 #pragma unroll
-    for (int h = 0; h < GM; ++h) {
+  for (int v = 0; v < NV; ++v) {
+    zt[v] = st.zacc[v];
+    zt[v] += shfl_xor(zt[v], 16);
+    zt[v] += shfl_xor(zt[v], 32);
+  }
+  __syncthreads();  // every wavefront is done with its staging region
+  float* s_o = reinterpret_cast<float*>(smem);  // [kWaves][8][D]
+  float* s_m = s_o + kWaves * 8 * D;            // [kWaves][8]
+  float* s_l = s_m + kWaves * 8;                // [kWaves][8]
+  float* s_z = s_l + kWaves * 8;                // [kWaves][8][4]
+  const bool quant_wg = BITS > 0 && !is_tail;
+  if (quad == 0 && rep == 0 && hilo == 0) {
+    s_m[wave * 8 + head] = st.m;
+    s_l[wave * 8 + head] = lt;
+    if (!quant_wg) {
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) s_o[wave][h][c0 + c] = o[h][c];
-      if (c0 == 0) {
-        s_ml[wave][h][0] = m[h];
-        s_ml[wave][h][1] = l[h];
+      for (int G = 0; G < NG; ++G) s_z[(wave * 8 + head) * 4 + G] = 0.0f;
+    }
+  }
+  if (quant_wg && quad == 0 && slot_ok) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int G = slot + v * SP;
+      if (G < NG) s_z[(wave * 8 + head) * 4 + G] = zt[v];
+    }
+  }
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    if (quant_wg) {
+      constexpr int B2 = BITS > 0 ? BITS : 2;
+      const float osc = __builtin_ldexpf(1.0f, 24 - B2 * ((ct % Cfg<D, B2>::PPD) % Cfg<D, B2>::PER));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * quad + i;
+        const int hp_ = r >> 1, rep_ = hp_ / g;
+        const int slot_ = 2 * rep_ + (r & 1);
+        if (rep_ < R8 && (ct / 2) % SP == slot_) s_o[(wave * 8 + hp_ % g) * D + 16 * ct + col] = st.O[ct][i] * osc;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const int hp_ = 2 * quad + i / 2;
+        if (hp_ < g) s_o[(wave * 8 + hp_) * D + 16 * ct + col] = st.O[ct][i] + st.O[ct][i + 1];
       }
     }
   }
@@ -241,14 +550,14 @@ __global__ __launch_bounds__(kThreads) void draft_valu_kernel(DraftArgs a) {
     const int h = t / D, d = t % D;
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][h][0]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w * 8 + h]);
     float L = 0.0f, O = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float mw = s_ml[w][h][0];
+      const float mw = s_m[w * 8 + h];
       const float f = mw == kNegInf ? 0.0f : fast_exp2(mw - M);
-      L += s_ml[w][h][1] * f;
-      O += s_o[w][h][d] * f;
+      L += s_l[w * 8 + h] * f;
+      O += (s_o[(w * 8 + h) * D + d] + s_z[(w * 8 + h) * 4 + d / 32]) * f;
     }
     const int hq = hk * g + h;
     if (a.splits == 1) {
@@ -284,25 +593,46 @@ __global__ void draft_combine_kernel(const float* __restrict__ ws, int splits, i
   if (lse != nullptr && d == 0) lse[row] = L > 0.0f ? (M + __log2f(L)) * kLn2 : kNegInf;
 }
 
-int plan_draft_splits(int units, int max_keys) {
-  const int target = 4 * num_cus();
-  int s = (target + units - 1) / units;
-  const int cap = (max_keys + 255) / 256;
-  if (s > cap) s = cap;
-  if (s < 1) s = 1;
-  return s;
+struct DraftPlan {
+  int main_splits, main_bpw, tail_splits, tail_bpw, splits;
+};
+
+constexpr int kTailBpw = 2 * kWaves;  // tail workgroups: up to 2 blocks per wavefront
+
+DraftPlan plan_draft(int units, int main_blocks, int tail_blocks) {
+  DraftPlan p{};
+  if (main_blocks > 0) {
+    const int target = 4 * num_cus();
+    int s = (target + units - 1) / units;
+    const int cap = (main_blocks + 2 * kWaves - 1) / (2 * kWaves);  // >= 2 blocks per wavefront
+    if (s > cap) s = cap;
+    if (s < 1) s = 1;
+    p.main_bpw = (main_blocks + s - 1) / s;
+    p.main_splits = (main_blocks + p.main_bpw - 1) / p.main_bpw;
+  }
+  p.tail_bpw = kTailBpw;
+  p.tail_splits = (tail_blocks + kTailBpw - 1) / kTailBpw;
+  p.splits = p.main_splits + p.tail_splits;
+  if (p.splits == 0) {  // no key at all: one empty workgroup writes o = 0
+    p.tail_splits = 1;
+    p.splits = 1;
+  }
+  return p;
 }
 
-template <int D, int GM>
+template <int D, int BITS, int NV>
 void launch_draft(const DraftArgs& a, dim3 grid, hipStream_t st) {
-  if (a.kind == VC_KV_QUANT) {
-    if (a.bits == 4)
-      draft_valu_kernel<D, GM, 4><<<grid, kThreads, 0, st>>>(a);
-    else
-      draft_valu_kernel<D, GM, 2><<<grid, kThreads, 0, st>>>(a);
-  } else {
-    draft_valu_kernel<D, GM, 0><<<grid, kThreads, 0, st>>>(a);
-  }
+  draft_mfma_kernel<D, BITS, NV><<<grid, kThreads, 0, st>>>(a);
+}
+
+template <int D, int NV>
+void launch_bits(const DraftArgs& a, int bits, dim3 grid, hipStream_t st) {
+  if (bits == 4)
+    launch_draft<D, 4, NV>(a, grid, st);
+  else if (bits == 2)
+    launch_draft<D, 2, NV>(a, grid, st);
+  else
+    launch_draft<D, 0, 1>(a, grid, st);
 }
 
 }  // namespace
@@ -312,8 +642,11 @@ using namespace vc;
 
 extern "C" size_t vc_draft_ws_bytes(int B, int Hq, int Hkv, int D, int max_keys) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_keys < 0) return 0;
-  const int s = plan_draft_splits(B * Hkv, max_keys);
-  const size_t need = s > 1 ? (size_t)s * B * Hq * (D + 2) * sizeof(float) : 0;
+  // upper bound over every split of max_keys between the compressed part and the tail
+  const int nb = (max_keys + 31) / 32;
+  const DraftPlan p = plan_draft(B * Hkv, nb, 0);
+  const int s = p.main_splits + (nb + kTailBpw - 1) / kTailBpw + 1;
+  const size_t need = (size_t)s * B * Hq * (D + 2) * sizeof(float);
   return need < 256 ? 256 : need;
 }
 
@@ -327,7 +660,6 @@ extern "C" int vc_draft_attn(const vc_kv_comp* comp, const vc_tail* tail, const 
   if (g > 8) return fail(VC_ERR_UNSUPPORTED, "vc_draft_attn: GQA group %d > 8", g);
   VC_CHECK(aligned(q, 16) && aligned(out, 16), "vc_draft_attn: q/out must be 16-byte aligned");
   DraftArgs a{};
-  a.kind = comp->kind;
   a.q = static_cast<const uint16_t*>(q);
   a.out = out;
   a.lse = lse;
@@ -336,6 +668,7 @@ extern "C" int vc_draft_attn(const vc_kv_comp* comp, const vc_tail* tail, const 
   a.Hkv = Hkv;
   a.g = g;
   a.scale_log2 = scale * kLog2e;
+  int bits = 0;
   switch (comp->kind) {
     case VC_KV_QUANT:
       VC_CHECK(comp->bits == 2 || comp->bits == 4, "vc_draft_attn: bits must be 2 or 4 (got %d)", comp->bits);
@@ -343,37 +676,37 @@ extern "C" int vc_draft_attn(const vc_kv_comp* comp, const vc_tail* tail, const 
                comp->n_quant);
       VC_CHECK(comp->n_quant == 0 || (comp->k_codes && comp->v_codes && comp->k_meta && comp->v_meta),
                "vc_draft_attn: null codes/meta");
-      VC_CHECK(aligned(comp->k_codes, 8) && aligned(comp->v_codes, 8) && aligned(comp->k_meta, 4) &&
-                   aligned(comp->v_meta, 4),
-               "vc_draft_attn: codes must be 8-byte and meta 4-byte aligned");
-      a.bits = comp->bits;
+      VC_CHECK(aligned(comp->k_codes, 16) && aligned(comp->v_codes, 16) && aligned(comp->k_meta, 4) &&
+                   aligned(comp->v_meta, 8),
+               "vc_draft_attn: codes must be 16-byte, K meta 4-byte and V meta 8-byte aligned");
+      bits = comp->bits;
       a.n_quant = comp->n_quant;
       a.n_main = comp->n_quant;
       a.k_codes = comp->k_codes;
       a.v_codes = comp->v_codes;
-      a.k_meta = static_cast<const H2*>(comp->k_meta);
-      a.v_meta = static_cast<const H2*>(comp->v_meta);
+      a.k_meta = static_cast<const uint32_t*>(comp->k_meta);
+      a.v_meta = static_cast<const uint32_t*>(comp->v_meta);
       break;
     case VC_KV_IDENTITY:
     case VC_KV_TOKEN_DROP:
       VC_CHECK(comp->L_cap >= 0, "vc_draft_attn: bad L_cap");
+      VC_CHECK(comp->L_full >= 0 && comp->L_full <= comp->L_cap, "vc_draft_attn: L_full=%d outside [0, L_cap=%d]",
+               comp->L_full, comp->L_cap);
       if (comp->kind == VC_KV_IDENTITY) {
-        VC_CHECK(comp->L_full >= 0 && comp->L_full <= comp->L_cap, "vc_draft_attn: L_full=%d outside [0, L_cap=%d]",
-                 comp->L_full, comp->L_cap);
         a.n_main = comp->L_full;
+        a.keep_idx = nullptr;
       } else {
         VC_CHECK(comp->n_keep >= 0, "vc_draft_attn: bad n_keep");
         VC_CHECK(comp->n_keep == 0 || comp->keep_idx != nullptr, "vc_draft_attn: null keep_idx");
         a.n_main = comp->n_keep;
+        a.keep_idx = comp->keep_idx;
       }
       VC_CHECK(a.n_main == 0 || (comp->k_full && comp->v_full), "vc_draft_attn: null k_full/v_full");
       VC_CHECK(aligned(comp->k_full, 16) && aligned(comp->v_full, 16), "vc_draft_attn: k_full/v_full misaligned");
       a.k_full = static_cast<const uint16_t*>(comp->k_full);
       a.v_full = static_cast<const uint16_t*>(comp->v_full);
-      a.L_full = comp->L_full;
       a.L_cap = comp->L_cap;
-      a.keep_idx = comp->keep_idx;
-      a.n_keep = comp->n_keep;
+      a.row_bound = comp->L_full;
       break;
     default:
       return fail(VC_ERR_INVALID, "vc_draft_attn: unknown compressor kind %d", comp->kind);
@@ -390,35 +723,35 @@ extern "C" int vc_draft_attn(const vc_kv_comp* comp, const vc_tail* tail, const 
     a.T_cap = 0;
   }
   const int units = B * Hkv;
-  const int max_keys = a.n_main + a.T_cap;
-  const int splits = plan_draft_splits(units, max_keys);
-  const size_t need = vc_draft_ws_bytes(B, Hq, Hkv, D, max_keys);
-  if (splits > 1) {
+  const int main_blocks = (a.n_main + 31) / 32;
+  const int tail_blocks = (a.T_cap + 31) / 32;
+  const DraftPlan p = plan_draft(units, main_blocks, tail_blocks);
+  const size_t need = (size_t)p.splits * B * Hq * (D + 2) * sizeof(float);
+  if (p.splits > 1) {
     if (ws == nullptr || ws_bytes < need)
       return fail(VC_ERR_WORKSPACE, "vc_draft_attn: workspace %zu < %zu bytes", ws_bytes, need);
     VC_CHECK(aligned(ws, 16), "vc_draft_attn: workspace misaligned");
   }
-  int kps = (max_keys + splits - 1) / splits;
-  kps = ((kps + 31) / 32) * 32;
-  if (kps == 0) kps = 32;
-  a.keys_per_split = kps;
-  a.splits = splits;
+  a.main_splits = p.main_splits;
+  a.main_bpw = p.main_bpw;
+  a.tail_bpw = p.tail_bpw;
+  a.splits = p.splits;
   a.ws = static_cast<float*>(ws);
-  dim3 grid(splits, units);
+  dim3 grid(p.splits, units);
+  // two V-group variants per lane are needed when fewer than NG slots exist per head
+  const int NG = D / 32, SP = 2 * (8 / g);
+  const int nv = bits > 0 && SP < NG ? 2 : 1;
   if (D == 128) {
-    if (g <= 4)
-      launch_draft<128, 4>(a, grid, stream);
+    if (nv == 2)
+      launch_bits<128, 2>(a, bits, grid, stream);
     else
-      launch_draft<128, 8>(a, grid, stream);
+      launch_bits<128, 1>(a, bits, grid, stream);
   } else {
-    if (g <= 4)
-      launch_draft<64, 4>(a, grid, stream);
-    else
-      launch_draft<64, 8>(a, grid, stream);
+    launch_bits<64, 1>(a, bits, grid, stream);
   }
   VC_HIP(hipGetLastError());
-  if (splits > 1) {
-    draft_combine_kernel<<<B * Hq, D, 0, stream>>>(a.ws, splits, B * Hq, D, out, lse);
+  if (p.splits > 1) {
+    draft_combine_kernel<<<B * Hq, D, 0, stream>>>(a.ws, p.splits, B * Hq, D, out, lse);
     VC_HIP(hipGetLastError());
   }
   return VC_OK;

@@ -75,10 +75,11 @@ __global__ void quant_k_kernel(const uint16_t* __restrict__ src, int L_cap, int 
   for (int i = 0; i < 32; ++i) out[(size_t)i * row_bytes] = (uint8_t)packed[i];
 }
 
-// V: groups of 32 channels of one token.  One thread per (token, group).
+// V: groups of 32 channels of one token.  Pass 1, one thread per (token, group):
+// the group's scale and zero.
 template <int BITS>
-__global__ void quant_v_kernel(const uint16_t* __restrict__ src, int L_cap, int D, int n_quant,
-                               uint8_t* __restrict__ codes, H2* __restrict__ meta) {
+__global__ void quant_v_meta_kernel(const uint16_t* __restrict__ src, int L_cap, int D, int n_quant,
+                                    H2* __restrict__ meta) {
   constexpr int QMAX = (1 << BITS) - 1;
   const int unit = blockIdx.y;
   const int G = D / 32;
@@ -86,32 +87,40 @@ __global__ void quant_v_kernel(const uint16_t* __restrict__ src, int L_cap, int 
   if (gid >= n_quant * G) return;
   const int t = gid / G, grp = gid % G;
   const uint16_t* row = src + ((size_t)unit * L_cap + t) * D + grp * 32;
-  float x[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) x[i] = bf16_to_f32(row[i]);
-  float mn = x[0], mx = x[0];
+  float mn = bf16_to_f32(row[0]), mx = mn;
 #pragma unroll
   for (int i = 1; i < 32; ++i) {
-    mn = fminf(mn, x[i]);
-    mx = fmaxf(mx, x[i]);
-  }
-  _Float16 sh, zh;
-  group_params(mn, mx, QMAX, sh, zh);
-  const float s = (float)sh, z = (float)zh;
-  const int row_bytes = D * BITS / 8;
-  uint8_t* out = codes + ((size_t)unit * n_quant + t) * row_bytes + grp * 32 * BITS / 8;
-  constexpr int PER = 8 / BITS;
-#pragma unroll
-  for (int byte = 0; byte < 32 / PER; ++byte) {
-    uint32_t v = 0;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) v |= code_of(x[byte * PER + e], s, z, QMAX) << (BITS * e);
-    out[byte] = (uint8_t)v;
+    const float x = bf16_to_f32(row[i]);
+    mn = fminf(mn, x);
+    mx = fmaxf(mx, x);
   }
   H2 m;
-  m.s = sh;
-  m.z = zh;
+  group_params(mn, mx, QMAX, m.s, m.z);
   meta[((size_t)unit * n_quant + t) * G + grp] = m;
+}
+
+// V pass 2, one thread per code byte of the tiled layout (vc_vcode_locate in
+// vc_common.h): the byte's codes all belong to one token.
+template <int BITS>
+__global__ void quant_v_pack_kernel(const uint16_t* __restrict__ src, int L_cap, int D, int n_quant,
+                                    const H2* __restrict__ meta, uint8_t* __restrict__ codes) {
+  constexpr int QMAX = (1 << BITS) - 1;
+  const int unit = blockIdx.y;
+  const int block_bytes = 4 * D * BITS;  // 32 tokens x D codes
+  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (n_quant / 32) * block_bytes) return;
+  const int blk = gid / block_bytes, byte = gid % block_bytes;
+  uint32_t v = 0;
+#pragma unroll
+  for (int k = 0; k < 8 / BITS; ++k) {
+    int tau, c;
+    vcode_inverse(D, BITS, byte, k, tau, c);
+    const int t = blk * 32 + tau;
+    const float x = bf16_to_f32(src[((size_t)unit * L_cap + t) * D + c]);
+    const H2 m = meta[((size_t)unit * n_quant + t) * (D / 32) + c / 32];
+    v |= code_of(x, (float)m.s, (float)m.z, QMAX) << (BITS * k);
+  }
+  codes[(size_t)unit * n_quant * D * BITS / 8 + gid] = (uint8_t)v;
 }
 
 __device__ __forceinline__ uint32_t unpack_code(const uint8_t* row, int d, int bits) {
@@ -124,8 +133,14 @@ __global__ void dequant_kernel(const uint8_t* __restrict__ codes, const H2* __re
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= n_quant * D) return;
   const int t = idx / D, d = idx % D;
-  const int row_bytes = D * bits / 8;
-  const uint32_t c = unpack_code(codes + (size_t)t * row_bytes, d, bits);
+  uint32_t c;
+  if (which == 0) {
+    c = unpack_code(codes + (size_t)t * (D * bits / 8), d, bits);
+  } else {
+    int byte, shift;
+    vcode_locate(D, bits, t % 32, d, byte, shift);
+    c = (codes[(size_t)(t / 32) * 4 * D * bits + byte] >> shift) & ((1u << bits) - 1u);
+  }
   const H2 m = which == 0 ? meta[(size_t)(t / 32) * D + d] : meta[(size_t)t * (D / 32) + d / 32];
   out[idx] = fmaf((float)c, (float)m.s, (float)m.z);
 }
@@ -144,6 +159,7 @@ extern "C" int vc_quantize_kv(const void* k_src, const void* v_src, int B, int H
   if (D != 64 && D != 128) return fail(VC_ERR_UNSUPPORTED, "vc_quantize_kv: D=%d not in {64,128}", D);
   const int nq = out->n_quant;
   VC_CHECK(nq >= 0 && nq % 32 == 0 && nq <= L_cap, "vc_quantize_kv: n_quant=%d must be a multiple of 32 <= L_cap", nq);
+  if (nq == 0) return VC_OK;
   VC_CHECK(k_src && v_src && out->k_codes && out->v_codes && out->k_meta && out->v_meta,
            "vc_quantize_kv: null pointer");
   VC_CHECK(aligned(k_src, 2) && aligned(v_src, 2) && aligned(out->k_meta, 4) && aligned(out->v_meta, 4),
@@ -160,12 +176,15 @@ extern "C" int vc_quantize_kv(const void* k_src, const void* v_src, int B, int H
   const int cols = D * out->bits / 8;
   const int G = D / 32;
   dim3 gv((nq * G + 255) / 256, units);
+  dim3 gp((nq / 32 * 4 * D * out->bits + 255) / 256, units);
   if (out->bits == 4) {
     quant_k_kernel<4><<<gk, cols, 0, stream>>>(ks, L_cap, D, nq, kc, km);
-    quant_v_kernel<4><<<gv, 256, 0, stream>>>(vs, L_cap, D, nq, vcodes, vm);
+    quant_v_meta_kernel<4><<<gv, 256, 0, stream>>>(vs, L_cap, D, nq, vm);
+    quant_v_pack_kernel<4><<<gp, 256, 0, stream>>>(vs, L_cap, D, nq, vm, vcodes);
   } else {
     quant_k_kernel<2><<<gk, cols, 0, stream>>>(ks, L_cap, D, nq, kc, km);
-    quant_v_kernel<2><<<gv, 256, 0, stream>>>(vs, L_cap, D, nq, vcodes, vm);
+    quant_v_meta_kernel<2><<<gv, 256, 0, stream>>>(vs, L_cap, D, nq, vm);
+    quant_v_pack_kernel<2><<<gp, 256, 0, stream>>>(vs, L_cap, D, nq, vm, vcodes);
   }
   VC_HIP(hipGetLastError());
   return VC_OK;

@@ -44,6 +44,45 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Lane shuffles inside a 64-wide wavefront.
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// ------------------------------------------------ tiled V code layout ---
+// V codes of 32 consecutive tokens (a "block") are stored as the B operands of
+// the draft kernel's P.V matrix product, so that one wavefront reads a block
+// with one coalesced load of D*bits/16 bytes per lane and unpacks it with bit
+// masks only.  Token tau (0..31) of a block and channel c (0..D-1) map to
+//   lane  = 16 * q + (c % 16)       with q = (tau % 16) / 4
+//   slot  e = tau % 4 + 4 * (tau / 16)   (k index of the 16x16x32 product)
+//   pair  i = e / 2, half hf = e % 2, column tile ct = c / 16
+//   pi    = i * (D / 16) + ct,   pairs per dword PPD = 16 / bits
+//   dword = pi / PPD, position j = pi % PPD
+//   bit   = bits * j + 16 * hf   inside that dword of the lane's chunk
+// A lane's chunk holds D*bits/16 bytes; chunks follow each other by lane, and
+// blocks by block index.  The two codes of a pair sit at bit b and b + 16 of
+// one dword, so masking the dword gives both as f16 bit patterns at once.
+__host__ __device__ inline void vcode_locate(int D, int bits, int tau, int c, int& byte, int& shift) {
+  const int q = (tau % 16) / 4, e = tau % 4 + 4 * (tau / 16);
+  const int lane = 16 * q + c % 16, i = e / 2, hf = e % 2, ct = c / 16;
+  const int pi = i * (D / 16) + ct, ppd = 16 / bits;
+  const int dword = pi / ppd, j = pi % ppd;
+  const int bit = bits * j + 16 * hf;
+  byte = lane * (D * bits / 16) + dword * 4 + bit / 8;
+  shift = bit % 8;
+}
+
+// Inverse of vcode_locate for the k-th code (k < 8 / bits) of block byte `byte`.
+__host__ __device__ inline void vcode_inverse(int D, int bits, int byte, int k, int& tau, int& c) {
+  const int lb = D * bits / 16;
+  const int lane = byte / lb, rem = byte % lb;
+  const int dword = rem / 4, bpos = rem % 4;
+  const int hf = bpos / 2;
+  const int bit = 8 * (bpos % 2) + bits * k;  // bit inside the 16-bit half
+  const int j = bit / bits;
+  const int pi = dword * (16 / bits) + j;
+  const int i = pi / (D / 16), ct = pi % (D / 16);
+  const int e = 2 * i + hf, q = lane / 16;
+  tau = e < 4 ? 4 * q + e : 16 + 4 * q + (e - 4);
+  c = 16 * ct + lane % 16;
+}
+
 struct Partial {  // split-K partial of one (row): unnormalised o, running max (log2 units), sum
   float m, l;
 };

@@ -55,12 +55,22 @@ extern "C" {
  *   k_codes  u8 [B][Hkv][n_quant][D*bits/8]  codes of token t packed along D:
  *            4-bit: channel 2i in the low nibble of byte i, 2i+1 in the high
  *            nibble; 2-bit: channel i at bit 2*(i%4) of byte i/4.
- *   v_codes  u8 [B][Hkv][n_quant][D*bits/8]  same packing.
+ *   v_codes  u8 [B][Hkv][n_quant/32][32*D*bits/8]  tiled: the codes of each
+ *            block of 32 tokens are laid out as the operands of the draft
+ *            kernel's matrix product.  Token tau (0..31) of a block, channel c:
+ *              q = (tau % 16) / 4, e = tau % 4 + 4 * (tau / 16),
+ *              lane = 16 q + c % 16, i = e / 2, hf = e % 2, ct = c / 16,
+ *              pi = i * (D/16) + ct, dword = pi / (16/bits), j = pi % (16/bits),
+ *              bit = bits * j + 16 * hf,
+ *              byte = lane * (D*bits/16) + 4 * dword + bit / 8,
+ *            code at bit (bit % 8) of that byte.  vc_quantize_kv writes it.
  *   k_meta   f16x2 [B][Hkv][n_quant/32][D]   {scale, zero} of the group formed
  *            by 32 consecutive tokens of one channel.
  *   v_meta   f16x2 [B][Hkv][n_quant][D/32]   {scale, zero} of the group formed
  *            by 32 consecutive channels of one token.
  *   Dequantised value = fp32(code * scale + zero), a single rounding.
+ *   Inputs must keep |q| * K scale < 4096 and |V| scale * 256 < 65504 (the
+ *   draft kernel carries these products in f16).
  * IDENTITY / TOKEN_DROP read k_full / v_full  bf16 [B][Hkv][L_cap][D]; rows
  *   [0, L_full) are context.  keep_idx int32 [B][Hkv][n_keep], sorted,
  *   each in [0, L_full); out-of-range entries are skipped, not dereferenced.
@@ -151,7 +161,8 @@ int vc_debug_dequant(const vc_kv_comp* comp, int B, int Hkv, int D, int b, int h
  *   out  device fp32 [B][Hq][D]
  *   lse  device fp32 [B][Hq] or NULL: natural log of sum_t exp(scale q.k_t)
  *   ws   device workspace of at least vc_draft_ws_bytes(B, Hq, Hkv, D,
- *        max keys) bytes, 256-byte aligned.  A sequence with no key at all
+ *        n_main + T_cap) bytes, 16-byte aligned (n_main = n_quant, L_full or
+ *        n_keep).  QUANT codes must be 16-byte aligned, V meta 8-byte.  A sequence with no key at all
  *        gets o = 0 and lse = -inf.
  * D in {64, 128}; Hq % Hkv == 0; Hq / Hkv <= 8.
  */

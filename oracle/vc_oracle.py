@@ -124,6 +124,38 @@ def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
     return out.astype(np.uint8)
 
 
+def pack_v_codes_tiled(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Pack V codes [n, D] (n % 32 == 0) into the tiled byte layout that the C
+    header (include/vc.h, QUANT layout, v_codes) defines; returns uint8
+    [n * D * bits / 8].  A pure permutation of the codes' bits, written from that
+    definition: token tau of each 32-token block and channel c go to
+      q = (tau % 16) // 4, e = tau % 4 + 4 (tau // 16), lane = 16 q + c % 16,
+      i = e // 2, hf = e % 2, ct = c // 16, pi = i (D / 16) + ct,
+      dword = pi // (16 / bits), j = pi % (16 / bits), bit = bits j + 16 hf,
+      byte = lane (D bits / 16) + 4 dword + bit // 8, shift = bit % 8."""
+    n, D = codes.shape
+    assert n % GROUP == 0
+    tau = np.arange(32)[:, None]
+    c = np.arange(D)[None, :]
+    q = (tau % 16) // 4
+    e = tau % 4 + 4 * (tau // 16)
+    lane = 16 * q + c % 16
+    i, hf, ct = e // 2, e % 2, c // 16
+    pi = i * (D // 16) + ct
+    ppd = 16 // bits
+    dword, j = pi // ppd, pi % ppd
+    bit = bits * j + 16 * hf
+    byte = lane * (D * bits // 16) + 4 * dword + bit // 8
+    shift = (bit % 8).astype(np.uint16)
+    nb = n // GROUP
+    blk_bytes = 4 * D * bits
+    out = np.zeros((nb, blk_bytes), dtype=np.uint16)
+    vals = codes.reshape(nb, 32, D).astype(np.uint16) << shift[None]
+    flat = (np.arange(nb)[:, None, None] * blk_bytes + byte[None]).reshape(-1)
+    np.bitwise_or.at(out.reshape(-1), flat, vals.reshape(-1))
+    return out.reshape(-1).astype(np.uint8)
+
+
 # ----------------------------------------------------------------------------
 # attention  [VC Core Algorithm: drafting with KV_comp, verification with KV_full]
 # ----------------------------------------------------------------------------

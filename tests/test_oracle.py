@@ -129,6 +129,39 @@ def test_pack_codes_bit_layout():
     assert list(O.pack_codes(c2, 2)[0]) == [0b00111001, 0xFF]
 
 
+def test_pack_v_tiled_positions_and_bijection():
+    """The tiled V layout (include/vc.h): hand-derived positions of single codes,
+    and every (token, channel) code lands on its own bits."""
+    D, bits = 128, 2
+    def where(tau, c, val=3):
+        codes = np.zeros((32, D), np.uint8)
+        codes[tau, c] = val
+        out = O.pack_v_codes_tiled(codes, bits)
+        nz = np.nonzero(out)[0]
+        assert len(nz) == 1
+        return int(nz[0]), int(out[nz[0]])
+    # tau 0, c 0: q 0, e 0, lane 0, pi 0 -> dword 0, bit 0
+    assert where(0, 0) == (0, 3)
+    # tau 1, c 0: e 1 -> hf 1 -> bit 16 -> byte 2
+    assert where(1, 0) == (2, 3)
+    # tau 17, c 16: q 0, e 5 -> i 2, hf 1; ct 1 -> pi 17 -> dword 2, j 1 -> bit 18 -> byte 10, shift 2
+    assert where(17, 16) == (10, 3 << 2)
+    # tau 6, c 37: q 1, e 2 -> i 1, hf 0; lane 16 + 5 = 21; ct 2 -> pi 10 -> dword 1, j 2 -> bit 4
+    assert where(6, 37) == (21 * 16 + 4, 3 << 4)
+    for D_, b_ in [(64, 2), (64, 4), (128, 2), (128, 4)]:
+        rng = np.random.default_rng(D_ + b_)
+        codes = rng.integers(0, 1 << b_, (64, D_)).astype(np.uint8)
+        packed = O.pack_v_codes_tiled(codes, b_)
+        assert packed.size == 64 * D_ * b_ // 8
+        # total bit population is preserved (no two codes share bits)
+        pop = lambda a: int(np.unpackbits(a.astype(np.uint8)).sum())
+        assert pop(packed) == pop(O.pack_codes(codes, b_))
+        # a permutation: each code value alone is found again
+        one = np.zeros_like(codes)
+        one[37, D_ - 3] = (1 << b_) - 1
+        assert pop(O.pack_v_codes_tiled(one, b_)) == b_
+
+
 def test_dequant_fraction_exact():
     rng = np.random.default_rng(2)
     codes = rng.integers(0, 16, (64, 64)).astype(np.uint8)

@@ -45,6 +45,12 @@ DRAFT_CASES = [
                  keep_frac=0.1, seed=25),
     C.TINY.with_(name="drop_d64_g4", B=1, Hq=4, Hkv=1, D=64, L=3000, k=2, kind="token_drop",
                  keep_frac=0.3, seed=26),
+    C.TINY.with_(name="int4_d128_g2_longtail", B=2, Hq=4, Hkv=2, D=128, L=1636, k=4, bits=4, residual=100,
+                 seed=27),
+    C.TINY.with_(name="int2_d128_g1", B=1, Hq=2, Hkv=2, D=128, L=2080, k=3, bits=2, residual=32, seed=28),
+    C.TINY.with_(name="int4_d64_allresidual", B=1, Hq=8, Hkv=2, D=64, L=96, k=3, bits=4, residual=96, seed=29),
+    C.TINY.with_(name="int2_d128_g4_splits", B=1, Hq=4, Hkv=1, D=128, L=16512, k=2, bits=2, residual=128,
+                 seed=30),
 ]
 
 
@@ -102,7 +108,7 @@ def test_quantize_bit_exact(D, bits):
             dq = vc.debug_dequant(comp, w.B, w.Hkv, D, b, h, 0).cpu().numpy()
             assert np.array_equal(dq.astype(np.float64), O.dequant_k(c, s, z)), (b, h, "k dequant")
             c, s, z = O.quantize_v(vf, bits)
-            assert np.array_equal(vcd[b, h], O.pack_codes(c, bits)), (b, h, "v codes")
+            assert np.array_equal(vcd[b, h].reshape(-1), O.pack_v_codes_tiled(c, bits)), (b, h, "v codes")
             assert np.array_equal(vm[b, h, ..., 0].view(np.uint16), s.view(np.uint16)), (b, h, "v scale")
             assert np.array_equal(vm[b, h, ..., 1].view(np.uint16), z.view(np.uint16)), (b, h, "v zero")
             dq = vc.debug_dequant(comp, w.B, w.Hkv, D, b, h, 1).cpu().numpy()
