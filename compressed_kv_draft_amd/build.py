@@ -19,6 +19,8 @@ FLAGS = [
     "-fno-gpu-flush-denormals-to-zero",
     # no packed-fp32 VALU instructions in any kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs (no AGPR copies around MFMA)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -56,7 +56,7 @@ struct DraftArgs {
   int main_splits, main_bpw;  // workgroups for the compressed part, blocks per workgroup
   int tail_bpw;               // blocks per tail workgroup
   int splits;                 // all workgroups of one (batch, kv-head)
-  float* ws;
+  float* ws;                  // split partials [splits][B][Hq][D + 2]
 };
 
 constexpr int kWaves = 4;
@@ -78,7 +78,7 @@ struct Cfg {
   static constexpr int VDW = D * B_ / 64;   // V code dwords per lane per block
   static constexpr int VMD = NG / 2;        // V meta dwords staged per lane per block
   static constexpr int VPITCH = D + 16;     // LDS row pitch (elements) of staged bf16 V
-  static constexpr int META_DW = BITS > 0 ? 2 * 16 * NKS + 32 * NG : 0;
+  static constexpr int META_DW = BITS > 0 ? 2 * 16 * NKS + 32 * NG + 8 : 0;  // + 8 zero dwords
   static constexpr int STAGE_BYTES = META_DW * 4 + 32 * VPITCH * 2;
   static constexpr int EPI_BYTES = kWaves * (8 * D + 8 + 8 + 8 * 4) * 4;
   static constexpr int SMEM = kWaves * STAGE_BYTES > EPI_BYTES ? kWaves * STAGE_BYTES : EPI_BYTES;
@@ -113,6 +113,11 @@ __device__ __forceinline__ void load_dwords(const void* p, uint32_t* out) {
       out[4 * k + 3] = w[3];
     }
   }
+}
+
+// Value of the neighbouring lane (lane ^ 1) through DPP quad_perm [1, 0, 3, 2].
+__device__ __forceinline__ float swap_adjacent(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
 }
 
 __device__ __forceinline__ float f16lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[0]; }
@@ -360,6 +365,8 @@ __global__ __launch_bounds__(kThreads) void draft_mfma_kernel(DraftArgs a) {
         for (int u = 0; u < C::VMD; ++u) r.vmt[u] = vmeta[(size_t)blk * 32 * NG + u];
       };
 
+      // lanes whose column has no V group read 8 zero dwords instead
+      if (lane < 8) vm[32 * NG + lane] = 0u;
       int blk = blo + wave;
       Raw cur;
       if (blk < bhi) load(blk, cur);
@@ -402,6 +409,8 @@ __global__ __launch_bounds__(kThreads) void draft_mfma_kernel(DraftArgs a) {
           qt[ks] = __builtin_bit_cast(f16x8, r4);
         }
         // code part of q.k for tokens col and 16 + col; hi + lo columns summed
+        const float code_scale = 0x1p20f * a.scale_log2;  // undoes 2^-24 (codes) * 2^kQExp (q)
+        const float zpart = accZ[0] * a.scale_log2;       // every row of accZ holds z . q
         float x[8];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -418,9 +427,8 @@ __global__ __launch_bounds__(kThreads) void draft_mfma_kernel(DraftArgs a) {
           }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float v = acc[i];
-            v += shfl_xor(v, 1);
-            x[4 * tt + i] = (v * 0x1p20f + accZ[i]) * a.scale_log2;
+            const float v = acc[i] + swap_adjacent(acc[i]);
+            x[4 * tt + i] = fmaf(v, code_scale, zpart);
           }
         }
         float P[8];
@@ -431,9 +439,9 @@ __global__ __launch_bounds__(kThreads) void draft_mfma_kernel(DraftArgs a) {
         for (int v = 0; v < NV; ++v) {
           const int G = slot + v * SP;
           const bool gok = slot_ok && G < NG;
-          const int Gc = gok ? G : 0;
-          const u32x4 m0 = *reinterpret_cast<const u32x4*>(vm + (Gc * 4 + quad) * 8);
-          const u32x4 m1 = *reinterpret_cast<const u32x4*>(vm + (Gc * 4 + quad) * 8 + 4);
+          const uint32_t* vmg = vm + (gok ? (G * 4 + quad) * 8 : 32 * NG);
+          const u32x4 m0 = *reinterpret_cast<const u32x4*>(vmg);
+          const u32x4 m1 = *reinterpret_cast<const u32x4*>(vmg + 4);
           const uint32_t mm[8] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
           float zs = 0.0f;
 #pragma unroll
@@ -442,10 +450,10 @@ __global__ __launch_bounds__(kThreads) void draft_mfma_kernel(DraftArgs a) {
             const float xs = P[e] * s;
             zs = fmaf(P[e], z, zs);
             const _Float16 h = (_Float16)xs;
-            Ahi[v][e] = gok ? h : (_Float16)0.0f;
-            Alo[v][e] = gok ? (_Float16)(xs - (float)h) : (_Float16)0.0f;
+            Ahi[v][e] = h;
+            Alo[v][e] = (_Float16)(xs - (float)h);
           }
-          st.zacc[v] += gok ? zs : 0.0f;
+          st.zacc[v] += zs;
         }
         // P.V code part
 #pragma unroll
@@ -574,23 +582,56 @@ __global__ __launch_bounds__(kThreads) void draft_mfma_kernel(DraftArgs a) {
   }
 }
 
-// Merge split partials (o unnormalised, m in log2 units, l) of every (b, h) row.
-__global__ void draft_combine_kernel(const float* __restrict__ ws, int splits, int rows, int D,
-                                     float* __restrict__ out, float* __restrict__ lse) {
+// Merge the split partials (o unnormalised, m in log2 units, l) of one (b, h)
+// row per workgroup: the splits' maxima and sums go through LDS, then every
+// thread reads its channel of all splits with independent loads.
+constexpr int kMaxCombineSplits = 256;
+__global__ __launch_bounds__(128) void draft_combine_kernel(const float* __restrict__ ws, int splits, int rows,
+                                                            int D, float* __restrict__ out,
+                                                            float* __restrict__ lse) {
+  __shared__ float s_f[kMaxCombineSplits], s_l[kMaxCombineSplits];
+  __shared__ float s_M, s_L;
   const int row = blockIdx.x;
-  const int d = threadIdx.x;
-  float M = kNegInf;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, ws[((size_t)s * rows + row) * (D + 2) + D]);
-  float L = 0.0f, O = 0.0f;
-  for (int s = 0; s < splits; ++s) {
+  for (int s = threadIdx.x; s < splits; s += blockDim.x) {
     const float* p = ws + ((size_t)s * rows + row) * (D + 2);
-    const float ms = p[D];
-    const float f = ms == kNegInf ? 0.0f : fast_exp2(ms - M);
-    L += p[D + 1] * f;
-    O += p[d] * f;
+    s_f[s] = p[D];
+    s_l[s] = p[D + 1];
   }
-  out[(size_t)row * D + d] = L > 0.0f ? O / L : 0.0f;
-  if (lse != nullptr && d == 0) lse[row] = L > 0.0f ? (M + __log2f(L)) * kLn2 : kNegInf;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    float M = kNegInf;
+    for (int s = threadIdx.x; s < splits; s += 64) M = fmaxf(M, s_f[s]);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
+    float L = 0.0f;
+    for (int s = threadIdx.x; s < splits; s += 64) {
+      const float f = s_f[s] == kNegInf ? 0.0f : fast_exp2(s_f[s] - M);
+      s_f[s] = f;
+      L += s_l[s] * f;
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) L += __shfl_xor(L, m, 64);
+    if (threadIdx.x == 0) {
+      s_M = M;
+      s_L = L;
+    }
+  }
+  __syncthreads();
+  const float L = s_L;
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float O = 0.0f;
+#pragma unroll 8
+    for (int s = 0; s < splits; ++s) O += ws[((size_t)s * rows + row) * (D + 2) + d] * s_f[s];
+    out[(size_t)row * D + d] = L > 0.0f ? O / L : 0.0f;
+  }
+  if (lse != nullptr && threadIdx.x == 0) lse[row] = L > 0.0f ? (s_M + __log2f(L)) * kLn2 : kNegInf;
+}
+
+// Workspace: the split partials.
+size_t draft_ws_need(int B, int Hq, int Hkv, int D, int splits) {
+  (void)Hkv;
+  const size_t need = (size_t)splits * B * Hq * (D + 2) * sizeof(float);
+  return need < 256 ? 256 : need;
 }
 
 struct DraftPlan {
@@ -646,8 +687,7 @@ extern "C" size_t vc_draft_ws_bytes(int B, int Hq, int Hkv, int D, int max_keys)
   const int nb = (max_keys + 31) / 32;
   const DraftPlan p = plan_draft(B * Hkv, nb, 0);
   const int s = p.main_splits + (nb + kTailBpw - 1) / kTailBpw + 1;
-  const size_t need = (size_t)s * B * Hq * (D + 2) * sizeof(float);
-  return need < 256 ? 256 : need;
+  return draft_ws_need(B, Hq, Hkv, D, s);
 }
 
 extern "C" int vc_draft_attn(const vc_kv_comp* comp, const vc_tail* tail, const void* q, float* out,
@@ -726,17 +766,18 @@ extern "C" int vc_draft_attn(const vc_kv_comp* comp, const vc_tail* tail, const 
   const int main_blocks = (a.n_main + 31) / 32;
   const int tail_blocks = (a.T_cap + 31) / 32;
   const DraftPlan p = plan_draft(units, main_blocks, tail_blocks);
-  const size_t need = (size_t)p.splits * B * Hq * (D + 2) * sizeof(float);
+  const size_t need = draft_ws_need(B, Hq, Hkv, D, p.splits);
   if (p.splits > 1) {
     if (ws == nullptr || ws_bytes < need)
       return fail(VC_ERR_WORKSPACE, "vc_draft_attn: workspace %zu < %zu bytes", ws_bytes, need);
     VC_CHECK(aligned(ws, 16), "vc_draft_attn: workspace misaligned");
+    VC_CHECK(p.splits <= kMaxCombineSplits, "vc_draft_attn: %d splits exceed %d", p.splits, kMaxCombineSplits);
+    a.ws = static_cast<float*>(ws);
   }
   a.main_splits = p.main_splits;
   a.main_bpw = p.main_bpw;
   a.tail_bpw = p.tail_bpw;
   a.splits = p.splits;
-  a.ws = static_cast<float*>(ws);
   dim3 grid(p.splits, units);
   // two V-group variants per lane are needed when fewer than NG slots exist per head
   const int NG = D / 32, SP = 2 * (8 / g);
@@ -751,7 +792,7 @@ extern "C" int vc_draft_attn(const vc_kv_comp* comp, const vc_tail* tail, const 
   }
   VC_HIP(hipGetLastError());
   if (p.splits > 1) {
-    draft_combine_kernel<<<B * Hq, D, 0, stream>>>(a.ws, p.splits, B * Hq, D, out, lse);
+    draft_combine_kernel<<<B * Hq, 128, 0, stream>>>(a.ws, p.splits, B * Hq, D, out, lse);
     VC_HIP(hipGetLastError());
   }
   return VC_OK;

@@ -102,7 +102,7 @@ class DeviceWorkload:
         self.q_steps = [self.q_verify[:, :, j, :].contiguous() for j in range(w.k)]
         self.scale = float(np.float32(1.0 / np.sqrt(w.D)))
         self.n_main = {"quant": w.n_quant, "token_drop": w.n_keep, "identity": w.L}[w.kind]
-        self.draft_ws = torch.empty(vc.draft_ws_bytes(w.B, w.Hq, w.Hkv, w.D, self.n_main + R + w.n_q),
+        self.draft_ws = torch.zeros(vc.draft_ws_bytes(w.B, w.Hq, w.Hkv, w.D, self.n_main + R + w.n_q),
                                     dtype=torch.uint8, device=device)
         self.verify_ws = torch.empty(vc.verify_ws_bytes(w.B, w.Hq, w.Hkv, w.D, w.n_q, w.L),
                                      dtype=torch.uint8, device=device)
