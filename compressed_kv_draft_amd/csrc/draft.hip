@@ -26,6 +26,9 @@
 // of 32-token blocks; wavefronts take every 4th block and keep their own
 // online-softmax state, merged in LDS at the end.  Workgroups past the main
 // splits handle the exact tail.  draft_combine_kernel merges the splits.
+#include <map>
+#include <mutex>
+
 #include "mfma.h"
 #include "vc_common.h"
 
@@ -133,18 +136,20 @@ struct State {
 };
 
 // Online softmax over the 8 scores a lane holds for one block (its head, tokens
-// 4q..4q+3 and 16+4q..16+4q+3).  The running max only moves when a score exceeds
-// it by kTau, so the accumulators are rescaled rarely; P <= 2^kTau.
+// 4q..4q+3 and 16+4q..16+4q+3).  Scores arrive relative to mu = m (0 while m is
+// still -inf).  The running max only moves when some score exceeds it by kTau, so
+// in the common case no cross-lane reduction and no rescale happen; P <= 2^kTau.
 template <int NCT, int NV>
-__device__ __forceinline__ void softmax_block(const float (&x)[8], State<NCT, NV>& st, float (&P)[8], int quad) {
-  float tmax = x[0];
+__device__ __forceinline__ void softmax_block(float (&x)[8], State<NCT, NV>& st, float (&P)[8], int quad) {
+  float tl = x[0];
 #pragma unroll
-  for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, x[e]);
-  tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-  tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-  const bool need = tmax > st.m + kTau;
+  for (int e = 1; e < 8; ++e) tl = fmaxf(tl, x[e]);
+  const bool need = st.m == kNegInf ? tl > kNegInf : tl > kTau;
   if (__any(need)) {
-    const float mn = fmaxf(st.m, tmax);
+    float tr = fmaxf(tl, shfl_xor(tl, 16));
+    tr = fmaxf(tr, shfl_xor(tr, 32));  // max over the head's tokens of this block
+    const float mu = st.m == kNegInf ? 0.0f : st.m;
+    const float mn = fmaxf(st.m, mu + tr);
     const float alpha = mn == kNegInf ? 1.0f : fast_exp2(st.m - mn);
     st.l *= alpha;
 #pragma unroll
@@ -156,17 +161,21 @@ __device__ __forceinline__ void softmax_block(const float (&x)[8], State<NCT, NV
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) st.O[ct][i] *= ar;
     }
+    const float delta = mn == kNegInf ? 0.0f : mn - mu;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] -= delta;
     st.m = mn;
   }
-  const float mu = st.m == kNegInf ? 0.0f : st.m;
   float ps = 0.0f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    P[e] = fast_exp2(x[e] - mu);
+    P[e] = fast_exp2(x[e]);
     ps += P[e];
   }
   st.l += ps;
 }
+
+__device__ __forceinline__ float mu_of(float m) { return m == kNegInf ? 0.0f : m; }
 
 // Source of exact bf16 rows: the tail, the identity cache or the kept rows.
 struct RowSrc {
@@ -215,7 +224,8 @@ __device__ __forceinline__ void rows_block(const RowSrc& src, int blk, const bf1
                               : u32x4{0u, 0u, 0u, 0u};
     *reinterpret_cast<u32x4*>(vst + row * VPITCH + off) = val;
   }
-  // scores (log2 units), invalid rows masked
+  // scores (log2 units, relative to the running max), invalid rows masked
+  const float mu = mu_of(st.m);
   float x[8];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
@@ -226,7 +236,7 @@ __device__ __forceinline__ void rows_block(const RowSrc& src, int blk, const bf1
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * tt + 4 * quad + i;
       const int pr = __shfl(myrow, r, 64);
-      x[4 * tt + i] = pr >= 0 ? acc[i] * scale_log2 : kNegInf;
+      x[4 * tt + i] = pr >= 0 ? fmaf(acc[i], scale_log2, -mu) : kNegInf;
     }
   }
   float P[8];
@@ -326,7 +336,12 @@ __global__ __launch_bounds__(kThreads) void draft_mfma_kernel(DraftArgs a) {
           }
         }
       }
-      const uint32_t lomask = hilo ? 0xFFFFFFFFu : 0u;
+      // qFm = qF in lo columns, 0 in hi columns
+      uint32_t qFm[NKS][4];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qFm[ks][i] = hilo ? qF[ks][i] : 0u;
       // K-meta pair this lane stages: (quad', ks', i') = lane
       const int nq32 = a.n_quant / 32;
       int kma = 0, kmb = 0;
@@ -402,15 +417,14 @@ __global__ __launch_bounds__(kThreads) void draft_mfma_kernel(DraftArgs a) {
             const uint32_t sw = s4[i];
             const f16x2 s = __builtin_bit_cast(f16x2, sw);
             const f16x2 qf = __builtin_bit_cast(f16x2, qF[ks][i]);
-            const f16x2 hi = qf * s;
-            const f16x2 t = __builtin_bit_cast(f16x2, __builtin_bit_cast(uint32_t, hi) & lomask);
-            r4[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qf, s, -t));
+            const f16x2 t = __builtin_bit_cast(f16x2, qFm[ks][i]) * s;  // RN(qF s) or 0
+            r4[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qf, s, -t));  // hi or lo
           }
           qt[ks] = __builtin_bit_cast(f16x8, r4);
         }
         // code part of q.k for tokens col and 16 + col; hi + lo columns summed
         const float code_scale = 0x1p20f * a.scale_log2;  // undoes 2^-24 (codes) * 2^kQExp (q)
-        const float zpart = accZ[0] * a.scale_log2;       // every row of accZ holds z . q
+        const float zpart = fmaf(accZ[0], a.scale_log2, -mu_of(st.m));  // rows of accZ all hold z . q
         float x[8];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -444,15 +458,19 @@ __global__ __launch_bounds__(kThreads) void draft_mfma_kernel(DraftArgs a) {
           const u32x4 m1 = *reinterpret_cast<const u32x4*>(vmg + 4);
           const uint32_t mm[8] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
           float zs = 0.0f;
+          u32x4 hi4, lo4;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float s = f16lo(mm[e]), z = f16hi(mm[e]);
-            const float xs = P[e] * s;
-            zs = fmaf(P[e], z, zs);
-            const _Float16 h = (_Float16)xs;
-            Ahi[v][e] = h;
-            Alo[v][e] = (_Float16)(xs - (float)h);
+          for (int k = 0; k < 4; ++k) {
+            const float x0 = P[2 * k] * f16lo(mm[2 * k]), x1 = P[2 * k + 1] * f16lo(mm[2 * k + 1]);
+            zs = fmaf(P[2 * k], f16hi(mm[2 * k]), zs);
+            zs = fmaf(P[2 * k + 1], f16hi(mm[2 * k + 1]), zs);
+            const auto h = __builtin_amdgcn_cvt_pkrtz(x0, x1);  // truncated hi; x - hi is exact
+            const auto l = __builtin_amdgcn_cvt_pkrtz(x0 - (float)h[0], x1 - (float)h[1]);
+            hi4[k] = __builtin_bit_cast(uint32_t, h);
+            lo4[k] = __builtin_bit_cast(uint32_t, l);
           }
+          Ahi[v] = __builtin_bit_cast(f16x8, hi4);
+          Alo[v] = __builtin_bit_cast(f16x8, lo4);
           st.zacc[v] += zs;
         }
         // P.V code part
@@ -640,11 +658,13 @@ struct DraftPlan {
 
 constexpr int kTailBpw = 2 * kWaves;  // tail workgroups: up to 2 blocks per wavefront
 
-DraftPlan plan_draft(int units, int main_blocks, int tail_blocks) {
+// wgs_per_cu: resident workgroups per CU of the kernel that will run; the main
+// part is sized to fill the chip exactly once.
+DraftPlan plan_draft(int units, int main_blocks, int tail_blocks, int wgs_per_cu) {
   DraftPlan p{};
   if (main_blocks > 0) {
-    const int target = 4 * num_cus();
-    int s = (target + units - 1) / units;
+    const int target = wgs_per_cu * num_cus();
+    int s = target / units;
     const int cap = (main_blocks + 2 * kWaves - 1) / (2 * kWaves);  // >= 2 blocks per wavefront
     if (s > cap) s = cap;
     if (s < 1) s = 1;
@@ -661,19 +681,29 @@ DraftPlan plan_draft(int units, int main_blocks, int tail_blocks) {
   return p;
 }
 
-template <int D, int BITS, int NV>
-void launch_draft(const DraftArgs& a, dim3 grid, hipStream_t st) {
-  draft_mfma_kernel<D, BITS, NV><<<grid, kThreads, 0, st>>>(a);
-}
+typedef void (*DraftKernel)(DraftArgs);
 
 template <int D, int NV>
-void launch_bits(const DraftArgs& a, int bits, dim3 grid, hipStream_t st) {
-  if (bits == 4)
-    launch_draft<D, 4, NV>(a, grid, st);
-  else if (bits == 2)
-    launch_draft<D, 2, NV>(a, grid, st);
-  else
-    launch_draft<D, 0, 1>(a, grid, st);
+DraftKernel pick_kernel(int bits) {
+  if (bits == 4) return draft_mfma_kernel<D, 4, NV>;
+  if (bits == 2) return draft_mfma_kernel<D, 2, NV>;
+  return draft_mfma_kernel<D, 0, 1>;
+}
+
+// Resident workgroups per CU of kernel k (cached per kernel and device).
+int wgs_per_cu(DraftKernel k) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  std::lock_guard<std::mutex> lk(mu);
+  auto key = std::make_pair(reinterpret_cast<const void*>(k), dev);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kThreads, 0) != hipSuccess || n < 1) n = 2;
+  cache[key] = n;
+  return n;
 }
 
 }  // namespace
@@ -685,7 +715,7 @@ extern "C" size_t vc_draft_ws_bytes(int B, int Hq, int Hkv, int D, int max_keys)
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_keys < 0) return 0;
   // upper bound over every split of max_keys between the compressed part and the tail
   const int nb = (max_keys + 31) / 32;
-  const DraftPlan p = plan_draft(B * Hkv, nb, 0);
+  const DraftPlan p = plan_draft(B * Hkv, nb, 0, 8);  // 8 resident workgroups per CU bound any kernel
   const int s = p.main_splits + (nb + kTailBpw - 1) / kTailBpw + 1;
   return draft_ws_need(B, Hq, Hkv, D, s);
 }
@@ -765,7 +795,12 @@ extern "C" int vc_draft_attn(const vc_kv_comp* comp, const vc_tail* tail, const 
   const int units = B * Hkv;
   const int main_blocks = (a.n_main + 31) / 32;
   const int tail_blocks = (a.T_cap + 31) / 32;
-  const DraftPlan p = plan_draft(units, main_blocks, tail_blocks);
+  // two V-group variants per lane are needed when fewer than NG slots exist per head
+  const int NG = D / 32, SP = 2 * (8 / g);
+  const int nv = bits > 0 && SP < NG ? 2 : 1;
+  const DraftKernel kern = D == 128 ? (nv == 2 ? pick_kernel<128, 2>(bits) : pick_kernel<128, 1>(bits))
+                                    : pick_kernel<64, 1>(bits);
+  const DraftPlan p = plan_draft(units, main_blocks, tail_blocks, wgs_per_cu(kern));
   const size_t need = draft_ws_need(B, Hq, Hkv, D, p.splits);
   if (p.splits > 1) {
     if (ws == nullptr || ws_bytes < need)
@@ -779,17 +814,7 @@ extern "C" int vc_draft_attn(const vc_kv_comp* comp, const vc_tail* tail, const 
   a.tail_bpw = p.tail_bpw;
   a.splits = p.splits;
   dim3 grid(p.splits, units);
-  // two V-group variants per lane are needed when fewer than NG slots exist per head
-  const int NG = D / 32, SP = 2 * (8 / g);
-  const int nv = bits > 0 && SP < NG ? 2 : 1;
-  if (D == 128) {
-    if (nv == 2)
-      launch_bits<128, 2>(a, bits, grid, stream);
-    else
-      launch_bits<128, 1>(a, bits, grid, stream);
-  } else {
-    launch_bits<64, 1>(a, bits, grid, stream);
-  }
+  kern<<<grid, kThreads, 0, stream>>>(a);
   VC_HIP(hipGetLastError());
   if (p.splits > 1) {
     draft_combine_kernel<<<B * Hq, 128, 0, stream>>>(a.ws, p.splits, B * Hq, D, out, lse);
