@@ -145,7 +145,7 @@ def main():
     draft_total = sum(d_ms) / a.steps
     verify_total = sum(v_ms) / a.steps
     dominant = "draft" if draft_total >= verify_total else "verify"
-    roof = {"bound": "hbm", "kernel": "vc_draft_attn (draft_valu_kernel + draft_combine_kernel)"
+    roof = {"bound": "hbm", "kernel": "vc_draft_attn (draft_mfma_kernel + draft_combine_kernel)"
             if dominant == "draft" else "vc_verify_attn (verify_mfma_kernel + verify_combine_kernel)",
             "achieved": round(d_gbs if dominant == "draft" else v_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round((d_gbs if dominant == "draft" else v_gbs) / HBM_PEAK_GBS, 4), "traffic": None,
@@ -156,12 +156,13 @@ def main():
         "metric": "verified tokens/sec per GPU; draft/verify attention HBM TB/s vs peak",
         "value": round(value, 1), "unit": "verified tokens/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
                    "context": w.L, "draft_len": w.k, "draft_cache": f"{w.kind}{w.bits if w.kind == 'quant' else ''}",
                    "residual": w.residual, "vocab": w.vocab, "layers_rotated": ROTATE,
                    "step": "k x vc_draft_attn + vc_verify_attn + vc_accept (one layer; vocab projection outside)",
-                   "arithmetic": "draft fp32 VALU; verify bf16/f16 MFMA, fp32 accumulate"},
+                   "arithmetic": "draft: int2 codes as exact f16 MFMA operands, q*s and p*s as f16 hi+lo; "
+                                 "verify: bf16 q.k, f16 p.v MFMA; fp32 accumulate and softmax"},
         "accept": {"n_accept": n.tolist(), "tokens_per_step": tokens_per_step,
                    "tokens_per_s_at_n_eq_k": round(w.B * w.n_q / step_s, 1),
                    "tokens_per_s_at_n_eq_25": round(w.B * 26 / step_s, 1)},

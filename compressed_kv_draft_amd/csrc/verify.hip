@@ -6,16 +6,22 @@
 //
 // The g query heads of a GQA group times the n_q positions form R = g * n_q
 // query rows that share one KV head, so q.K^T and P.V are real contractions.
-// A workgroup (4 wavefronts) owns one (batch, kv-head), one group of row tiles
-// and one split of the keys.  Per 32-key tile the workgroup stages K (bf16,
-// row-major) and V^T (converted to f16, keys permuted to the MFMA operand
-// order) in LDS once; each wavefront then runs, for each of its 16-row tiles,
-//   S^T[32 keys x 16 rows] = K . Q^T    (bf16 MFMA, fp32 accumulate)
-//   online softmax per row (all of a row's state lives in one lane column)
-//   O^T[D x 16 rows]     += V^T . P^T  (f16 MFMA, fp32 accumulate)
-// Computing the transposed products keeps a row's scores, softmax state and
-// output accumulators in the same lanes, so no data moves between lanes except
-// the 2-step max reduction over the 4 lanes of a column.
+// Per 32-key tile a workgroup (4 wavefronts) stages K (bf16, padded rows) and
+// V (converted to f16) in LDS once; every wavefront owns up to MT 16-row query
+// tiles and computes, for each,
+//   S[32 keys x 16 rows] = K . Q^T   (bf16 MFMA: keys are the A rows, so each
+//                                     lane ends up with 8 keys of one row)
+//   online softmax per row in fp32 (lazy rescale, running max moves by >= 2^8)
+//   O[16 rows x D]     += P . V      (f16 MFMA; P rounded to nearest even; V
+//                                     read transposed with ds_read_b64_tr_b16)
+// The K and V operands of a tile are read from LDS once per wavefront and
+// shared by its query tiles.  LDS is double-buffered with one barrier per tile;
+// the next tile's global loads are in flight during the current tile's math.
+// Query rows beyond 3 tiles per wavefront go to further row groups, laid out so
+// that the row groups of one key range run on the same XCD (shared L2).
+#include <map>
+#include <mutex>
+
 #include "mfma.h"
 #include "vc_common.h"
 
@@ -24,7 +30,9 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTile = 32;
+constexpr int kKT = 32;       // keys per tile
+constexpr int kMaxMT = 3;     // query tiles per wavefront
+constexpr float kTau = 8.0f;  // lazy rescale threshold (log2 units)
 
 struct VerifyArgs {
   const uint16_t* q;
@@ -39,8 +47,10 @@ struct VerifyArgs {
   int max_ctx;
   float* out;
   float* ws;
-  int B, Hq, Hkv, g, n_q, R, NT, tiles_per_group;
+  int B, Hq, Hkv, g, n_q, R, NT;
+  int rowgroups, tiles_per_group;  // query tiles per workgroup = kWaves * MT
   int splits, keys_per_split;
+  int n_su;                        // splits * units
   float scale_log2;
 };
 
@@ -58,76 +68,73 @@ __device__ __forceinline__ const uint16_t* row_ptr(const VerifyArgs& a, int b, i
   return a.k + (size_t)slot * page_elems + ((size_t)(hk * 2 + kv) * pt + (key & (pt - 1))) * D;
 }
 
-// Position of key kk (0..31 in the tile) in the permuted P^T / V^T operand order:
-// lane group jj = (kk % 16) / 4 holds keys {4jj + i, 16 + 4jj + i}, i < 4.
-__device__ __forceinline__ int perm_slot(int kk) {
-  const int mt = kk >> 4, w = kk & 15;
-  return (w >> 2) * 8 + mt * 4 + (w & 3);
+// 8 bf16 (one 16-byte chunk) -> 8 f16, round to nearest even.
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 w) {
+  u32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const f16x2 h = {(_Float16)bf16_lo(w[e]), (_Float16)bf16_hi(w[e])};
+    r[e] = __builtin_bit_cast(uint32_t, h);
+  }
+  return r;
 }
 
-template <int D, int MAXT>
+template <int D, int MT>
 __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
-  constexpr int KS = D / 32;   // k-steps of the q.k contraction
-  constexpr int DT = D / 16;   // 16-row tiles of O^T
-  constexpr int KPAD = D + 8;  // LDS row pitch (elements) of K
-  constexpr int VPAD = kTile + 8;
-  constexpr int CH = kTile * D / 8;            // 16-byte chunks per tile
+  constexpr int NKS = D / 32, NCT = D / 16;
+  constexpr int KP = D + 8;                          // K row pitch (elements)
+  constexpr int VP = D + 16;                         // V row pitch (elements)
+  constexpr int CH = kKT * D / 8;                    // 16-byte chunks per tile (K or V)
   constexpr int CPT = (CH + kThreads - 1) / kThreads;  // chunks per thread
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKT * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kKT * VP];
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kTile * KPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VPAD];
-
-  const int unit = blockIdx.y;
-  const int b = unit / a.Hkv;
-  const int hk = unit % a.Hkv;
-  const int split = blockIdx.x;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int col = lane & 15;
-  const int quad = lane >> 4;
+  // workgroup -> (row group, split, unit): the row groups of one (split, unit)
+  // are 8 workgroups apart, i.e. on the same XCD under round-robin dispatch
+  const int id = blockIdx.x;
+  const int x8 = id % 8, y = id / 8;
+  const int rg = y % a.rowgroups;
+  const int su = (y / a.rowgroups) * 8 + x8;
+  if (su >= a.n_su) return;
+  const int split = su % a.splits, unit = su / a.splits;
+  const int b = unit / a.Hkv, hk = unit % a.Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, quad = lane >> 4;
 
   int ctx = a.ctx_len[b];
   ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
-
-  // rows of this workgroup and the last key any of them may see
-  const int tile0 = blockIdx.z * a.tiles_per_group;
-  const int r_lo = tile0 * 16;
-  int r_hi = (tile0 + a.tiles_per_group) * 16;
-  r_hi = r_hi < a.R ? r_hi : a.R;
-  int jmax = a.n_q - 1;
-  if (r_hi - r_lo <= a.n_q && r_lo / a.n_q == (r_hi - 1) / a.n_q) jmax = (r_hi - 1) % a.n_q;
-  const int key_end = ctx + jmax + 1;
+  const int key_end = ctx + a.n_q;
   const int kb = split * a.keys_per_split;
-  int ke = kb + a.keys_per_split;
-  ke = ke < key_end ? ke : key_end;
+  const int ke = min(kb + a.keys_per_split, key_end);
 
-  // per-wavefront row tiles: tile0 + wave + 4 * i, below tile_end
+  // this wavefront's query tiles: tile0 + wave + kWaves * i
+  const int tile0 = rg * a.tiles_per_group;
   const int tile_end = min(tile0 + a.tiles_per_group, a.NT);
-  bf16x8 qb[MAXT][KS];
-  f32x4 acc[MAXT][DT];
-  float mrow[MAXT], lrow[MAXT];
-  int rlim[MAXT];  // last visible key of this lane's row, -1 if the row is padding
+  bf16x8 qb[MT][NKS];
+  f32x4 O[MT][NCT];
+  float m[MT], l[MT];
+  int rlim[MT];
 #pragma unroll
-  for (int i = 0; i < MAXT; ++i) {
+  for (int i = 0; i < MT; ++i) {
     const int tile = tile0 + wave + kWaves * i;
     const int r = tile * 16 + col;
-    const bool live = tile < tile_end && r < a.R;
     rlim[i] = -1;
-    if (live) {
+    if (tile < tile_end && r < a.R) {
       const int hl = r / a.n_q, j = r % a.n_q;
       rlim[i] = ctx + j;
-      const uint16_t* qp = a.q + ((size_t)(b * a.Hq + hk * a.g + hl) * a.n_q + j) * D + quad * 8;
+      const uint16_t* qp = a.q + ((size_t)(b * a.Hq + hk * a.g + hl) * a.n_q + j) * D + quad * (D / 4);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qb[i][ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
+      for (int ks = 0; ks < NKS; ++ks) qb[i][ks] = *reinterpret_cast<const bf16x8*>(qp + 8 * ks);
     } else {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qb[i][ks] = bf16x8{};
+      for (int ks = 0; ks < NKS; ++ks) qb[i][ks] = bf16x8{};
     }
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[i][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mrow[i] = kNegInf;
-    lrow[i] = 0.0f;
+    for (int ct = 0; ct < NCT; ++ct) O[i][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[i] = kNegInf;
+    l[i] = 0.0f;
   }
+  const bool wave_live = tile0 + wave < tile_end;
 
   // register staging of one tile: chunk c -> key c / (D/8), 8 channels at (c % (D/8)) * 8
   u32x4 kreg[CPT], vreg[CPT];
@@ -135,15 +142,14 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int c = threadIdx.x + u * kThreads;
-      kreg[u] = u32x4{0, 0, 0, 0};
-      vreg[u] = u32x4{0, 0, 0, 0};
+      kreg[u] = u32x4{0u, 0u, 0u, 0u};
+      vreg[u] = u32x4{0u, 0u, 0u, 0u};
       if (c < CH) {
-        const int kk = c / (D / 8), c8 = c % (D / 8);
-        const int key = t0 + kk;
+        const int key = t0 + c / (D / 8), c8 = c % (D / 8);
         if (key < ke) {
           const uint16_t* kp = row_ptr<D>(a, b, hk, key, 0);
-          const uint16_t* vp = row_ptr<D>(a, b, hk, key, 1);
           if (kp != nullptr) {
+            const uint16_t* vp = row_ptr<D>(a, b, hk, key, 1);
             kreg[u] = *reinterpret_cast<const u32x4*>(kp + c8 * 8);
             vreg[u] = *reinterpret_cast<const u32x4*>(vp + c8 * 8);
           }
@@ -151,183 +157,244 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
       }
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int c = threadIdx.x + u * kThreads;
       if (c < CH) {
         const int kk = c / (D / 8), c8 = c % (D / 8);
-        *reinterpret_cast<u32x4*>(&Ks[kk * KPAD + c8 * 8]) = kreg[u];
-        const int slot = perm_slot(kk);
-        const u32x4 w = vreg[u];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t x = w[e];
-          const _Float16 lo = (_Float16)__uint_as_float(x << 16);
-          const _Float16 hi = (_Float16)__uint_as_float(x & 0xFFFF0000u);
-          Vt[(c8 * 8 + 2 * e) * VPAD + slot] = __builtin_bit_cast(uint16_t, lo);
-          Vt[(c8 * 8 + 2 * e + 1) * VPAD + slot] = __builtin_bit_cast(uint16_t, hi);
-        }
+        *reinterpret_cast<u32x4*>(&Ks[buf][kk * KP + c8 * 8]) = kreg[u];
+        *reinterpret_cast<u32x4*>(&Vs[buf][kk * VP + c8 * 8]) = bf16x8_to_f16x8(vreg[u]);
       }
     }
   };
 
-  if (kb < ke) load_tile(kb);
-  for (int t0 = kb; t0 < ke; t0 += kTile) {
-    __syncthreads();  // previous tile fully consumed
-    store_tile();
-    __syncthreads();
-    if (t0 + kTile < ke) load_tile(t0 + kTile);
-
+  const int ntiles = ke > kb ? (ke - kb + kKT - 1) / kKT : 0;
+  if (ntiles > 0) {
+    load_tile(kb);
+    store_tile(0);
+    if (ntiles > 1) load_tile(kb + kKT);
+  }
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    const int t0 = kb + t * kKT;
+    if (t + 1 < ntiles) store_tile(buf ^ 1);  // its reads finished before the last barrier
+    if (t + 2 < ntiles) load_tile(t0 + 2 * kKT);
+    if (wave_live) {
+      // scores for every query tile; K operands read once, shared by the tiles
+      f32x4 s[MT][2];
 #pragma unroll
-    for (int i = 0; i < MAXT; ++i) {
-      if (tile0 + wave + kWaves * i >= tile_end) continue;  // wave-uniform
-      // S^T for the two 16-key halves of the tile
-      f32x4 s[2];
+      for (int i = 0; i < MT; ++i) s[i][0] = s[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        f32x4 c4 = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Ks[(mt * 16 + col) * KPAD + ks * 32 + quad * 8]);
-          c4 = mfma_bf16(av, qb[i][ks], c4);
-        }
-        s[mt] = c4;
-      }
-      // mask, scale, online softmax (row = this lane's column)
-      float tmax = kNegInf;
+        for (int ks = 0; ks < NKS; ++ks) {
+          const bf16x8 ka =
+              *reinterpret_cast<const bf16x8*>(&Ks[buf][(16 * h + col) * KP + quad * (D / 4) + 8 * ks]);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = t0 + mt * 16 + quad * 4 + e;
-          const bool ok = key <= rlim[i] && key < ke;
-          const float x = ok ? s[mt][e] * a.scale_log2 : kNegInf;
-          s[mt][e] = x;
-          tmax = fmaxf(tmax, x);
+          for (int i = 0; i < MT; ++i)
+            if (tile0 + wave + kWaves * i < tile_end) s[i][h] = mfma_bf16(ka, qb[i][ks], s[i][h]);
         }
       }
-      tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-      const float mnew = fmaxf(mrow[i], tmax);
-      const float muse = mnew == kNegInf ? 0.0f : mnew;
-      const float alpha = fast_exp2(mrow[i] - muse);
-      mrow[i] = mnew;
-      f16x8 pb;
-      float psum = 0.0f;
+      // mask only tiles that reach the drafted rows or the end of the range
+      const bool need_mask = t0 + kKT > ctx || t0 + kKT > ke;
+      f16x8 A[MT];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = fast_exp2(s[mt][e] - muse);
-          const _Float16 ph = (_Float16)p;  // round to nearest even
-          psum += (float)ph;                // sum the rounded weights actually applied
-          pb[mt * 4 + e] = ph;
+      for (int i = 0; i < MT; ++i) {
+        if (tile0 + wave + kWaves * i >= tile_end) {
+          A[i] = f16x8{};
+          continue;
         }
-      }
-      lrow[i] = lrow[i] * alpha + psum;
+        const float mu = m[i] == kNegInf ? 0.0f : m[i];
+        float xv[8];
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        acc[i][dt] *= alpha;
-        const f16x8 av = *reinterpret_cast<const f16x8*>(&Vt[(dt * 16 + col) * VPAD + quad * 8]);
-        acc[i][dt] = mfma_f16(av, pb, acc[i][dt]);
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float v = fmaf(s[i][h][e], a.scale_log2, -mu);
+            if (need_mask) {
+              const int key = t0 + 16 * h + 4 * quad + e;
+              if (key > rlim[i] || key >= ke) v = kNegInf;
+            }
+            xv[4 * h + e] = v;
+          }
+        float tl = xv[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) tl = fmaxf(tl, xv[e]);
+        const bool need = m[i] == kNegInf ? tl > kNegInf : tl > kTau;
+        if (__any(need)) {
+          float tr = fmaxf(tl, shfl_xor(tl, 16));
+          tr = fmaxf(tr, shfl_xor(tr, 32));
+          const float mn = fmaxf(m[i], mu + tr);
+          const float alpha = mn == kNegInf ? 1.0f : fast_exp2(m[i] - mn);
+          l[i] *= alpha;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float ar = __shfl(alpha, 4 * quad + e, 64);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) O[i][ct][e] *= ar;
+          }
+          const float delta = mn == kNegInf ? 0.0f : mn - mu;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xv[e] -= delta;
+          m[i] = mn;
+        }
+        float ps = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = fast_exp2(xv[e]);
+          ps += p;
+          A[i][e] = (_Float16)p;  // round to nearest even
+        }
+        l[i] += ps;
+      }
+      // P . V: V operands read once per column tile, shared by the query tiles
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const uint16_t* base = &Vs[buf][16 * ct + 4 * (col & 3)];
+        const s16x4 lo4 = lds_read_tr16(base + (4 * quad + (col >> 2)) * VP);
+        const s16x4 hi4 = lds_read_tr16(base + (16 + 4 * quad + (col >> 2)) * VP);
+        const f16x8 bv = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+          if (tile0 + wave + kWaves * i < tile_end) O[i][ct] = mfma_f16(A[i], bv, O[i][ct]);
       }
     }
+    __syncthreads();
   }
 
-  // finalise: total row sum over the 4 lanes of the column, then write
+  // finalise: the row sum over the 4 lanes of a column, then write o (or the
+  // split partial).  Output row 4q+e of O belongs to query row (tile*16 + 4q+e),
+  // whose max and sum live in the lanes with col == 4q+e.
 #pragma unroll
-  for (int i = 0; i < MAXT; ++i) {
-    float lt = lrow[i];
+  for (int i = 0; i < MT; ++i) {
+    const int tile = tile0 + wave + kWaves * i;
+    if (tile >= tile_end) continue;  // wave-uniform
+    float lt = l[i];
     lt += shfl_xor(lt, 16);
     lt += shfl_xor(lt, 32);
-    if (rlim[i] < 0) continue;
-    const int r = (tile0 + wave + kWaves * i) * 16 + col;
-    const int hl = r / a.n_q, j = r % a.n_q;
-    const size_t row = (size_t)(b * a.Hq + hk * a.g + hl) * a.n_q + j;
-    if (a.splits == 1) {
-      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-      float* op = a.out + row * D + quad * 4;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        f32x4 v = acc[i][dt] * inv;
-        *reinterpret_cast<f32x4*>(op + dt * 16) = v;
-      }
-    } else {
-      const size_t rows = (size_t)a.B * a.Hq * a.n_q;
-      float* pp = a.ws + ((size_t)split * rows + row) * (D + 2);
+    for (int e = 0; e < 4; ++e) {
+      const int rr = 4 * quad + e;
+      const float le = __shfl(lt, rr, 64);
+      const float me = __shfl(m[i], rr, 64);
+      const int r = tile * 16 + rr;
+      if (r >= a.R) continue;
+      const int hl = r / a.n_q, j = r % a.n_q;
+      const size_t row = (size_t)(b * a.Hq + hk * a.g + hl) * a.n_q + j;
+      if (a.splits == 1) {
+        const float inv = le > 0.0f ? 1.0f / le : 0.0f;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        float* dst = pp + dt * 16 + quad * 4;
-        dst[0] = acc[i][dt][0];
-        dst[1] = acc[i][dt][1];
-        dst[2] = acc[i][dt][2];
-        dst[3] = acc[i][dt][3];
-      }
-      if (quad == 0) {
-        pp[D] = mrow[i];
-        pp[D + 1] = lt;
+        for (int ct = 0; ct < NCT; ++ct) a.out[row * D + 16 * ct + col] = O[i][ct][e] * inv;
+      } else {
+        const size_t rows = (size_t)a.B * a.Hq * a.n_q;
+        float* pp = a.ws + ((size_t)split * rows + row) * (D + 2);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) pp[16 * ct + col] = O[i][ct][e];
+        if (col == 0) {
+          pp[D] = me;
+          pp[D + 1] = le;
+        }
       }
     }
   }
 }
 
-__global__ void verify_combine_kernel(const float* __restrict__ ws, int splits, int rows, int D,
-                                      float* __restrict__ out) {
+// Merge split partials of one query row per workgroup (see draft_combine_kernel).
+constexpr int kMaxCombineSplits = 256;
+__global__ __launch_bounds__(128) void verify_combine_kernel(const float* __restrict__ ws, int splits, int rows,
+                                                             int D, float* __restrict__ out) {
+  __shared__ float s_f[kMaxCombineSplits], s_l[kMaxCombineSplits];
+  __shared__ float s_L;
   const int row = blockIdx.x;
-  const int d = threadIdx.x;
-  float M = kNegInf;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, ws[((size_t)s * rows + row) * (D + 2) + D]);
-  float L = 0.0f, O = 0.0f;
-  for (int s = 0; s < splits; ++s) {
+  for (int s = threadIdx.x; s < splits; s += blockDim.x) {
     const float* p = ws + ((size_t)s * rows + row) * (D + 2);
-    const float ms = p[D];
-    const float f = ms == kNegInf ? 0.0f : fast_exp2(ms - M);
-    L += p[D + 1] * f;
-    O += p[d] * f;
+    s_f[s] = p[D];
+    s_l[s] = p[D + 1];
   }
-  out[(size_t)row * D + d] = L > 0.0f ? O / L : 0.0f;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    float M = kNegInf;
+    for (int s = threadIdx.x; s < splits; s += 64) M = fmaxf(M, s_f[s]);
+#pragma unroll
+    for (int mm = 32; mm >= 1; mm >>= 1) M = fmaxf(M, __shfl_xor(M, mm, 64));
+    float L = 0.0f;
+    for (int s = threadIdx.x; s < splits; s += 64) {
+      const float f = s_f[s] == kNegInf ? 0.0f : fast_exp2(s_f[s] - M);
+      s_f[s] = f;
+      L += s_l[s] * f;
+    }
+#pragma unroll
+    for (int mm = 32; mm >= 1; mm >>= 1) L += __shfl_xor(L, mm, 64);
+    if (threadIdx.x == 0) s_L = L;
+  }
+  __syncthreads();
+  const float L = s_L;
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float O = 0.0f;
+#pragma unroll 8
+    for (int s = 0; s < splits; ++s) O += ws[((size_t)s * rows + row) * (D + 2) + d] * s_f[s];
+    out[(size_t)row * D + d] = L > 0.0f ? O / L : 0.0f;
+  }
+}
+
+typedef void (*VerifyKernel)(VerifyArgs);
+
+template <int D>
+VerifyKernel pick(int mt) {
+  if (mt == 1) return verify_mfma_kernel<D, 1>;
+  if (mt == 2) return verify_mfma_kernel<D, 2>;
+  return verify_mfma_kernel<D, 3>;
+}
+
+int wgs_per_cu(VerifyKernel k) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  std::lock_guard<std::mutex> lk(mu);
+  auto key = std::make_pair(reinterpret_cast<const void*>(k), dev);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kThreads, 0) != hipSuccess || n < 1) n = 2;
+  cache[key] = n;
+  return n;
 }
 
 struct Plan {
-  int maxt, tiles_per_group, groups, splits, kps;
+  int mt, tiles_per_group, rowgroups, splits, kps;
 };
 
-Plan plan_verify(int B, int Hq, int Hkv, int n_q, int max_ctx) {
+// wpc: resident workgroups per CU of the kernel (8 bounds every variant).
+Plan plan_verify(int B, int Hq, int Hkv, int n_q, int max_ctx, int wpc) {
   Plan p{};
   const int g = Hq / Hkv;
   const int R = g * n_q;
   const int NT = (R + 15) / 16;
-  int maxt = (NT + kWaves - 1) / kWaves;
-  if (maxt > 4 && NT > 5 * kWaves) maxt = 4;
-  if (maxt > 5) maxt = 5;
-  p.maxt = maxt;
-  p.tiles_per_group = maxt * kWaves;
-  p.groups = (NT + p.tiles_per_group - 1) / p.tiles_per_group;
-  const int units = B * Hkv * p.groups;
+  p.rowgroups = (NT + kWaves * kMaxMT - 1) / (kWaves * kMaxMT);
+  const int per_group = (NT + p.rowgroups - 1) / p.rowgroups;
+  p.mt = (per_group + kWaves - 1) / kWaves;
+  p.tiles_per_group = per_group;
+  const int units = B * Hkv * p.rowgroups;
   const int keys = max_ctx + n_q;
-  const int target = 2 * num_cus();
-  int s = (target + units - 1) / units;
-  const int cap = (keys + 255) / 256;
+  const int target = wpc * num_cus();
+  int s = target / units;
+  const int cap = (keys + 4 * kKT - 1) / (4 * kKT);  // >= 4 tiles per split
   if (s > cap) s = cap;
   if (s < 1) s = 1;
   int kps = (keys + s - 1) / s;
-  kps = ((kps + kTile - 1) / kTile) * kTile;
+  kps = ((kps + kKT - 1) / kKT) * kKT;
   s = (keys + kps - 1) / kps;
   p.splits = s;
   p.kps = kps;
   return p;
 }
 
-template <int D>
-void launch_verify(const VerifyArgs& a, int maxt, dim3 grid, hipStream_t st) {
-  switch (maxt) {
-    case 1: verify_mfma_kernel<D, 1><<<grid, kThreads, 0, st>>>(a); break;
-    case 2: verify_mfma_kernel<D, 2><<<grid, kThreads, 0, st>>>(a); break;
-    case 3: verify_mfma_kernel<D, 3><<<grid, kThreads, 0, st>>>(a); break;
-    case 4: verify_mfma_kernel<D, 4><<<grid, kThreads, 0, st>>>(a); break;
-    default: verify_mfma_kernel<D, 5><<<grid, kThreads, 0, st>>>(a); break;
-  }
+size_t verify_ws_need(int B, int Hq, int n_q, int D, int splits) {
+  const size_t need = splits > 1 ? (size_t)splits * B * Hq * n_q * (D + 2) * sizeof(float) : 0;
+  return need < 256 ? 256 : need;
 }
 
 }  // namespace
@@ -337,9 +404,8 @@ using namespace vc;
 
 extern "C" size_t vc_verify_ws_bytes(int B, int Hq, int Hkv, int D, int n_q, int max_ctx) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0 || n_q <= 0 || max_ctx < 0) return 0;
-  const Plan p = plan_verify(B, Hq, Hkv, n_q, max_ctx);
-  const size_t need = p.splits > 1 ? (size_t)p.splits * B * Hq * n_q * (D + 2) * sizeof(float) : 0;
-  return need < 256 ? 256 : need;
+  const Plan p = plan_verify(B, Hq, Hkv, n_q, max_ctx, 8);
+  return verify_ws_need(B, Hq, n_q, D, p.splits);
 }
 
 extern "C" int vc_verify_attn(const void* q, const vc_kv_full* kv, const int32_t* ctx_len, int max_ctx, int n_q,
@@ -384,26 +450,29 @@ extern "C" int vc_verify_attn(const void* q, const vc_kv_full* kv, const int32_t
   a.R = a.g * n_q;
   a.NT = (a.R + 15) / 16;
   a.scale_log2 = scale * kLog2e;
-  const Plan p = plan_verify(B, Hq, Hkv, n_q, max_ctx);
+  Plan p = plan_verify(B, Hq, Hkv, n_q, max_ctx, 8);
+  const VerifyKernel kern = D == 128 ? pick<128>(p.mt) : pick<64>(p.mt);
+  p = plan_verify(B, Hq, Hkv, n_q, max_ctx, wgs_per_cu(kern));
+  a.rowgroups = p.rowgroups;
   a.tiles_per_group = p.tiles_per_group;
   a.splits = p.splits;
   a.keys_per_split = p.kps;
+  a.n_su = p.splits * B * Hkv;
   if (p.splits > 1) {
-    const size_t need = vc_verify_ws_bytes(B, Hq, Hkv, D, n_q, max_ctx);
+    const size_t need = verify_ws_need(B, Hq, n_q, D, p.splits);
     if (ws == nullptr || ws_bytes < need)
       return fail(VC_ERR_WORKSPACE, "vc_verify_attn: workspace %zu < %zu bytes", ws_bytes, need);
     VC_CHECK(aligned(ws, 16), "vc_verify_attn: workspace misaligned");
+    VC_CHECK(p.splits <= kMaxCombineSplits, "vc_verify_attn: %d splits exceed %d", p.splits, kMaxCombineSplits);
     a.ws = static_cast<float*>(ws);
   }
-  dim3 grid(p.splits, B * Hkv, p.groups);
-  if (D == 128)
-    launch_verify<128>(a, p.maxt, grid, stream);
-  else
-    launch_verify<64>(a, p.maxt, grid, stream);
+  // 1-D grid: 8 consecutive (split, unit) pairs per group of 8 * rowgroups workgroups
+  const int n_wg = ((a.n_su + 7) / 8) * 8 * p.rowgroups;
+  kern<<<n_wg, kThreads, 0, stream>>>(a);
   VC_HIP(hipGetLastError());
   if (p.splits > 1) {
     const int rows = B * Hq * n_q;
-    verify_combine_kernel<<<rows, D, 0, stream>>>(a.ws, p.splits, rows, D, out);
+    verify_combine_kernel<<<rows, 128, 0, stream>>>(a.ws, p.splits, rows, D, out);
     VC_HIP(hipGetLastError());
   }
   return VC_OK;
