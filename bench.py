@@ -31,7 +31,128 @@ def parse():
     p.add_argument("--config", default="llama3_8b_layer_b8_l32k_int2_k32")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-units", type=int, default=8, help="(b, kv-head) units in the CPU oracle sample")
+    p.add_argument("--stagger", action="store_true",
+                   help="measure the full-KV prefetch of one request group against the other group's drafting "
+                        "(Llama-70B-shaped paged workload) and print that JSON line instead")
     return p.parse_args()
+
+
+def stagger(a):
+    """Cross-resource staggering on one GPU: group B's full KV (shuffled 16-token
+    pages, pinned host pool) streams to the device pool on a copy stream while
+    group A runs its k draft steps on the compute stream.  Times draft alone,
+    copy alone and both together; overlap = (t_d + t_c - t_both) / min(t_d, t_c)."""
+    import numpy as np
+    import torch
+
+    import compressed_kv_draft_amd as vc
+    from compressed_kv_draft_amd import workload as WL
+    from synth import configs as C
+    from synth import inputs as I
+
+    w = C.LLAMA70B
+    bg = w.B // w.groups
+    torch.cuda.set_device(0)
+    # group A: its int4 draft cache (contiguous) and tail
+    wa = w.with_(B=bg, paged=False)
+    dw = WL.DeviceWorkload(wa, device="cuda:0", with_vocab=False)
+    # group B: the paged full KV of sequences bg .. 2bg-1 in a pinned host pool
+    table, n_slots = I.page_table(w)
+    page_bytes = w.Hkv * 2 * w.page_tokens * w.D * 2
+    host = torch.empty(n_slots * page_bytes, dtype=torch.uint8)
+    host.fill_(0x3C)
+    seqs = list(range(bg, 2 * bg))
+    chunks = [(t, min(t + w.chunk_tokens, w.L)) for t in range(0, w.L, w.chunk_tokens)]
+    pages_per_chunk = len(seqs) * (w.chunk_tokens // w.page_tokens)
+    n_pages = pages_per_chunk * len(chunks)
+    copy_bytes = n_pages * page_bytes
+    chunk_bytes = pages_per_chunk * page_bytes
+    # group B's device region: its chunks one after the other (a device page
+    # table for the paged verify points here)
+    dev_region = torch.empty(copy_bytes, dtype=torch.uint8, device="cuda:0")
+    staging = [torch.empty(chunk_bytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+    done = [torch.cuda.Event(), torch.cuda.Event()]
+    comp = torch.cuda.current_stream()
+    cps = torch.cuda.Stream()
+
+    def drafts():
+        for j in range(w.k):
+            dw.draft_step(j)
+
+    def copies():
+        for c, (t0, t1) in enumerate(chunks):
+            vc.prefetch_full_kv(host, page_bytes, table, seqs, t0, t1, w.page_tokens, staging[c % 2],
+                                dev_region[c * chunk_bytes:(c + 1) * chunk_bytes], stream=cps,
+                                done_event=done[c % 2], staging_free=done[c % 2] if c >= 2 else None)
+
+    def timed(fn, stream):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1), 1e3 * (time.perf_counter() - t0)
+
+    drafts()
+    copies()
+    torch.cuda.synchronize()
+    # the k draft steps as one HIP graph: one submission from the host
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        drafts()
+    torch.cuda.synchronize()
+    drafts_eager = drafts
+
+    def drafts():
+        graph.replay()
+
+    graph.replay()
+    torch.cuda.synchronize()
+    ref = dw.draft_out.clone()
+    drafts_eager()
+    torch.cuda.synchronize()
+    if not torch.equal(ref, dw.draft_out):
+        raise RuntimeError("graph replay of the draft steps differs from eager execution")
+    reps = max(1, a.steps)
+    td = float(np.median([timed(drafts, comp)[0] for _ in range(reps)]))
+    tc = float(np.median([timed(copies, cps)[1] for _ in range(reps)]))   # wall: includes the host gather
+    big = staging[0]
+    tref = float(np.median([timed(lambda: dev_region[:chunk_bytes].copy_(big, non_blocking=True), comp)[0]
+                            for _ in range(reps)]))
+    import threading
+    both, d_in = [], []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        # the prefetch runs on its own host thread (its gathers and copy submissions
+        # release the GIL), as a serving runtime's prefetcher would
+        th = threading.Thread(target=copies)
+        th.start()
+        dA0, dA1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        dA0.record(comp)
+        drafts()
+        dA1.record(comp)
+        th.join()
+        torch.cuda.synchronize()
+        both.append(1e3 * (time.perf_counter() - t0))
+        d_in.append(dA0.elapsed_time(dA1))
+    tb = float(np.median(both))
+    tdi = float(np.median(d_in))
+    overlap = (td + tc - tb) / min(td, tc)
+    line = {"metric": "full-KV prefetch overlap with draft compute (cross-resource staggering, one GPU)",
+            "value": round(overlap, 4), "unit": "fraction of the shorter activity hidden", "n_gpus": 1,
+            "steps": reps, "higher_is_better": True, "data": "synthetic",
+            "config": {"workload": w.name + "_stagger", "draft_group": f"seqs 0..{bg - 1}, int4, k={w.k}",
+                       "prefetch_group": f"seqs {bg}..{2 * bg - 1}, {len(chunks)} chunks of {w.chunk_tokens} "
+                                         f"tokens, {n_pages} shuffled pages of {page_bytes} B"},
+            "t_draft_ms": round(td, 3), "t_copy_ms": round(tc, 3), "t_both_ms": round(tb, 3),
+            "draft_under_copy_ms": round(tdi, 3), "draft_slowdown": round(tdi / td, 4),
+            "prefetch_GBps": round(copy_bytes / tc / 1e6, 2),
+            "pcie_GBps_one_chunk_copy": round(chunk_bytes / tref / 1e6, 2),
+            "copy_bytes": int(copy_bytes)}
+    print(json.dumps(line), flush=True)
 
 
 def cpu_baseline(w, dw, n_accept_sum, units):
@@ -73,6 +194,9 @@ def main():
         print(f"bench.py runs on one GPU only: the hot path is per-GPU data parallel with no exchange; "
               f"--gpus {a.gpus} is not supported.", file=sys.stderr)
         sys.exit(2)
+    if a.stagger:
+        stagger(a)
+        return
     import numpy as np
     import torch
 

@@ -52,8 +52,8 @@ EXPORTS = {
                                c_int, c_int, c_int, c_int, c_float, c_void, c_size, c_void]),
     "vc_argmax": (c_int, [c_void, c_int, c_int, c_void, c_void]),
     "vc_accept": (c_int, [c_void, c_void, c_int, c_int, c_int, c_void, c_void, c_void]),
-    "vc_prefetch_full_kv": (c_int, [c_void, c_void, c_size, c_int, c_void, c_int, c_int, c_void, c_int,
-                                    c_int, c_int, c_int, c_void, c_void]),
+    "vc_prefetch_full_kv": (c_int, [c_void, c_size, c_int, c_void, c_int, c_int, c_void, c_int,
+                                    c_int, c_int, c_int, c_void, c_size, c_void, c_void, c_void, c_void]),
 }
 
 
@@ -245,19 +245,26 @@ def accept(draft_ids: torch.Tensor, verify_logits: torch.Tensor, out_ids=None, n
 
 # ------------------------------------------------------------------ prefetch
 
-def prefetch_full_kv(host_pool: torch.Tensor, dev_pool: torch.Tensor, page_bytes: int, page_table_host,
-                     seq_ids, tok_begin: int, tok_end: int, page_tokens: int, stream=None, done_event=None):
-    """host_pool: pinned CPU uint8 [slots * page_bytes]; page_table_host: int32 numpy [n_seq, pages]."""
+def prefetch_full_kv(host_pool: torch.Tensor, page_bytes: int, page_table_host, seq_ids, tok_begin: int,
+                     tok_end: int, page_tokens: int, staging: torch.Tensor, dev_dst: torch.Tensor, stream=None,
+                     done_event=None, staging_free=None):
+    """host_pool: CPU uint8 [slots * page_bytes]; page_table_host: int32 numpy [n_seq, pages];
+    staging: pinned CPU uint8; dev_dst: device uint8.  Pages land in dev_dst in
+    (sequence, page) order."""
     import numpy as np
     tab = np.ascontiguousarray(page_table_host, dtype=np.int32)
     seqs = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int32))
-    n_slots = dev_pool.numel() // page_bytes
-    if host_pool.numel() < n_slots * page_bytes:
-        raise VcError(f"host pool holds {host_pool.numel()} bytes < {n_slots} slots * {page_bytes}")
+    n_slots = host_pool.numel() // page_bytes
+    p0 = tok_begin // page_tokens
+    p1 = (tok_end + page_tokens - 1) // page_tokens
+    need = len(seqs) * (p1 - p0) * page_bytes
+    if dev_dst.numel() < need:
+        raise VcError(f"dev_dst holds {dev_dst.numel()} bytes < {need}")
     ev = c_void(done_event.cuda_event) if done_event is not None else None
+    fr = c_void(staging_free.cuda_event) if staging_free is not None else None
     s = torch.cuda.current_stream() if stream is None else stream
-    rc = LIB.vc_prefetch_full_kv(c_void(host_pool.data_ptr()), _ptr(dev_pool), page_bytes, n_slots,
-                                 tab.ctypes.data_as(c_void), tab.shape[0], tab.shape[1],
-                                 seqs.ctypes.data_as(c_void), len(seqs), tok_begin, tok_end, page_tokens,
-                                 c_void(s.cuda_stream), ev)
+    rc = LIB.vc_prefetch_full_kv(c_void(host_pool.data_ptr()), page_bytes, n_slots, tab.ctypes.data_as(c_void),
+                                 tab.shape[0], tab.shape[1], seqs.ctypes.data_as(c_void), len(seqs), tok_begin,
+                                 tok_end, page_tokens, c_void(staging.data_ptr()), staging.numel(),
+                                 _ptr(dev_dst), fr, c_void(s.cuda_stream), ev)
     _check(rc, "vc_prefetch_full_kv")

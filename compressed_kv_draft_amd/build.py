@@ -28,7 +28,7 @@ FLAGS = [
 def build(verbose: bool = True) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIB + ".tmp"
-    cmd = ["hipcc", *FLAGS, "-o", tmp, *srcs]
+    cmd = ["hipcc", *FLAGS, "-o", tmp, *srcs, "-ldl"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -21,6 +21,7 @@
 // that the row groups of one key range run on the same XCD (shared L2).
 #include <map>
 #include <mutex>
+#include <type_traits>
 
 #include "mfma.h"
 #include "vc_common.h"
@@ -54,20 +55,6 @@ struct VerifyArgs {
   float scale_log2;
 };
 
-// Address of row `key` (K if kv == 0, V if kv == 1) of (b, hk), or nullptr.
-template <int D>
-__device__ __forceinline__ const uint16_t* row_ptr(const VerifyArgs& a, int b, int hk, int key, int kv) {
-  if (a.page_table == nullptr) {
-    const uint16_t* base = kv == 0 ? a.k : a.v;
-    return base + ((size_t)(b * a.Hkv + hk) * a.L_cap + key) * D;
-  }
-  const int pt = 1 << a.page_log2;
-  const int slot = a.page_table[(size_t)b * a.pages_per_seq + (key >> a.page_log2)];
-  if (slot < 0 || slot >= a.n_slots) return nullptr;
-  const size_t page_elems = (size_t)a.Hkv * 2 * pt * D;
-  return a.k + (size_t)slot * page_elems + ((size_t)(hk * 2 + kv) * pt + (key & (pt - 1))) * D;
-}
-
 // 8 bf16 (one 16-byte chunk) -> 8 f16, round to nearest even.
 __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 w) {
   u32x4 r;
@@ -79,7 +66,7 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 w) {
   return r;
 }
 
-template <int D, int MT>
+template <int D, int MT, bool PAGED>
 __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
   constexpr int NKS = D / 32, NCT = D / 16;
   constexpr int KP = D + 8;                          // K row pitch (elements)
@@ -136,51 +123,68 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
   }
   const bool wave_live = tile0 + wave < tile_end;
 
-  // register staging of one tile: chunk c -> key c / (D/8), 8 channels at (c % (D/8)) * 8
-  u32x4 kreg[CPT], vreg[CPT];
-  auto load_tile = [&](int t0) {
+  // register staging, two tiles deep: chunk c -> key c / (D/8), 8 channels at (c % (D/8)) * 8
+  int ck[CPT], cc[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int c = threadIdx.x + u * kThreads;
+    ck[u] = c < CH ? c / (D / 8) : kKT;  // kKT: never a valid key offset
+    cc[u] = (c % (D / 8)) * 8;
+  }
+  const size_t unit_row0 = (size_t)(b * a.Hkv + hk) * a.L_cap;
+  const int pt_mask = (1 << a.page_log2) - 1;
+  const size_t page_elems = (size_t)a.Hkv * 2 * (pt_mask + 1) * D;
+  u32x4 kreg[2][CPT], vreg[2][CPT];
+  auto load_tile = [&](int t0, int set) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const int c = threadIdx.x + u * kThreads;
-      kreg[u] = u32x4{0u, 0u, 0u, 0u};
-      vreg[u] = u32x4{0u, 0u, 0u, 0u};
-      if (c < CH) {
-        const int key = t0 + c / (D / 8), c8 = c % (D / 8);
-        if (key < ke) {
-          const uint16_t* kp = row_ptr<D>(a, b, hk, key, 0);
-          if (kp != nullptr) {
-            const uint16_t* vp = row_ptr<D>(a, b, hk, key, 1);
-            kreg[u] = *reinterpret_cast<const u32x4*>(kp + c8 * 8);
-            vreg[u] = *reinterpret_cast<const u32x4*>(vp + c8 * 8);
+      const int key = t0 + ck[u];
+      kreg[set][u] = u32x4{0u, 0u, 0u, 0u};
+      vreg[set][u] = u32x4{0u, 0u, 0u, 0u};
+      if (ck[u] < kKT && key < ke) {
+        if constexpr (PAGED) {
+          const int slot = a.page_table[(size_t)b * a.pages_per_seq + (key >> a.page_log2)];
+          if (slot >= 0 && slot < a.n_slots) {
+            const uint16_t* kp =
+                a.k + (size_t)slot * page_elems + ((size_t)(hk * 2) * (pt_mask + 1) + (key & pt_mask)) * D + cc[u];
+            kreg[set][u] = *reinterpret_cast<const u32x4*>(kp);
+            vreg[set][u] = *reinterpret_cast<const u32x4*>(kp + (size_t)(pt_mask + 1) * D);
           }
+        } else {
+          const size_t off = (unit_row0 + key) * D + cc[u];
+          kreg[set][u] = *reinterpret_cast<const u32x4*>(a.k + off);
+          vreg[set][u] = *reinterpret_cast<const u32x4*>(a.v + off);
         }
       }
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf, int set) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int c = threadIdx.x + u * kThreads;
       if (c < CH) {
         const int kk = c / (D / 8), c8 = c % (D / 8);
-        *reinterpret_cast<u32x4*>(&Ks[buf][kk * KP + c8 * 8]) = kreg[u];
-        *reinterpret_cast<u32x4*>(&Vs[buf][kk * VP + c8 * 8]) = bf16x8_to_f16x8(vreg[u]);
+        *reinterpret_cast<u32x4*>(&Ks[buf][kk * KP + c8 * 8]) = kreg[set][u];
+        *reinterpret_cast<u32x4*>(&Vs[buf][kk * VP + c8 * 8]) = bf16x8_to_f16x8(vreg[set][u]);
       }
     }
   };
 
+  // tile t sits in register set t & 1 until it is stored to LDS buffer t & 1 at
+  // the start of iteration t - 1; its loads were issued in iteration t - 3.
   const int ntiles = ke > kb ? (ke - kb + kKT - 1) / kKT : 0;
   if (ntiles > 0) {
-    load_tile(kb);
-    store_tile(0);
-    if (ntiles > 1) load_tile(kb + kKT);
+    load_tile(kb, 0);
+    store_tile(0, 0);
+    if (ntiles > 1) load_tile(kb + kKT, 1);
+    if (ntiles > 2) load_tile(kb + 2 * kKT, 0);
   }
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+  // one tile; `buf` is a literal at each call so register sets index statically
+  auto step = [&](int t, const int buf) __attribute__((always_inline)) {
     const int t0 = kb + t * kKT;
-    if (t + 1 < ntiles) store_tile(buf ^ 1);  // its reads finished before the last barrier
-    if (t + 2 < ntiles) load_tile(t0 + 2 * kKT);
+    if (t + 1 < ntiles) store_tile(buf ^ 1, buf ^ 1);  // LDS buffer read before the last barrier
+    if (t + 3 < ntiles) load_tile(t0 + 3 * kKT, buf ^ 1);
     if (wave_live) {
       // scores for every query tile; K operands read once, shared by the tiles
       f32x4 s[MT][2];
@@ -211,14 +215,16 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float v = fmaf(s[i][h][e], a.scale_log2, -mu);
-            if (need_mask) {
-              const int key = t0 + 16 * h + 4 * quad + e;
-              if (key > rlim[i] || key >= ke) v = kNegInf;
-            }
-            xv[4 * h + e] = v;
-          }
+          for (int e = 0; e < 4; ++e) xv[4 * h + e] = fmaf(s[i][h][e], a.scale_log2, -mu);
+        if (need_mask) {
+          // key t0 + 16h + 4q + e is visible iff 16h + e <= lim
+          const int lim = min(rlim[i], ke - 1) - t0 - 4 * quad;
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (16 * h + e > lim) xv[4 * h + e] = kNegInf;
+        }
         float tl = xv[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) tl = fmaxf(tl, xv[e]);
@@ -262,6 +268,10 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
       }
     }
     __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, 0);
+    if (t + 1 < ntiles) step(t + 1, 1);
   }
 
   // finalise: the row sum over the 4 lanes of a column, then write o (or the
@@ -341,11 +351,11 @@ __global__ __launch_bounds__(128) void verify_combine_kernel(const float* __rest
 
 typedef void (*VerifyKernel)(VerifyArgs);
 
-template <int D>
+template <int D, bool PAGED>
 VerifyKernel pick(int mt) {
-  if (mt == 1) return verify_mfma_kernel<D, 1>;
-  if (mt == 2) return verify_mfma_kernel<D, 2>;
-  return verify_mfma_kernel<D, 3>;
+  if (mt == 1) return verify_mfma_kernel<D, 1, PAGED>;
+  if (mt == 2) return verify_mfma_kernel<D, 2, PAGED>;
+  return verify_mfma_kernel<D, 3, PAGED>;
 }
 
 int wgs_per_cu(VerifyKernel k) {
@@ -451,7 +461,9 @@ extern "C" int vc_verify_attn(const void* q, const vc_kv_full* kv, const int32_t
   a.NT = (a.R + 15) / 16;
   a.scale_log2 = scale * kLog2e;
   Plan p = plan_verify(B, Hq, Hkv, n_q, max_ctx, 8);
-  const VerifyKernel kern = D == 128 ? pick<128>(p.mt) : pick<64>(p.mt);
+  const bool paged = kv->page_table != nullptr;
+  const VerifyKernel kern = D == 128 ? (paged ? pick<128, true>(p.mt) : pick<128, false>(p.mt))
+                                     : (paged ? pick<64, true>(p.mt) : pick<64, false>(p.mt));
   p = plan_verify(B, Hq, Hkv, n_q, max_ctx, wgs_per_cu(kern));
   a.rowgroups = p.rowgroups;
   a.tiles_per_group = p.tiles_per_group;

@@ -221,25 +221,33 @@ int vc_accept(const int32_t* draft_ids, const float* verify_logits, int B, int k
               int32_t* out_ids, int32_t* n_accept, hipStream_t stream);
 
 /*
- * vc_prefetch_full_kv — stream the full-KV pages of tokens [tok_begin,
- * tok_end) of the listed sequences from a pinned host pool into the device
- * pool, as host-to-device DMA copies on copy_stream, then record `done` (if
- * not NULL) on copy_stream.  [VC Architecture Support: long-context decoding
- * keeps the full KV in CPU memory and loads it over PCIe for verification;
- * VC Key System Innovations P1: the load overlaps other requests' drafting]
- *   host_pool  pinned host memory (hipHostMalloc), slots * page_bytes bytes
- *   dev_pool   device memory of the same slot layout
- *   page_table host int32 [n_seq_total][pages_per_seq]; slot of logical page
- *              p of sequence b (same slot in both pools); slots < n_slots
- *   seq_ids    host int32 [n_seq]
- * Pages p in [tok_begin / page_tokens, ceil(tok_end / page_tokens)) are copied;
- * runs of consecutive slots are merged into one copy.  No kernels run.
- * An unpinned host_pool is rejected with VC_ERR_INVALID.
+ * vc_prefetch_full_kv — move the full-KV pages of tokens [tok_begin, tok_end)
+ * of the listed sequences from the host pool to device memory with one
+ * host-to-device DMA copy on copy_stream, then record `done` (if not NULL) on
+ * copy_stream.  [VC Architecture Support: long-context decoding keeps the full
+ * KV in CPU memory and loads it over PCIe for verification; VC Key System
+ * Innovations P1: the load overlaps other requests' drafting]
+ *   host_pool    host memory of n_slots pages of page_bytes; logical page p of
+ *                sequence b sits in slot page_table[b * pages_per_seq + p]
+ *   page_table   host int32 [n_seq_total][pages_per_seq], slots < n_slots
+ *   seq_ids      host int32 [n_seq]
+ *   staging      pinned host memory (hipHostMalloc) of at least
+ *                n_seq * n_pages * page_bytes, n_pages = ceil(tok_end /
+ *                page_tokens) - tok_begin / page_tokens
+ *   staging_free host waits on this event (if not NULL) before writing staging:
+ *                pass the `done` of the previous copy out of the same buffer
+ *   dev_dst      device memory of the same size
+ * Host threads gather the pages into staging in order (sequence i of seq_ids,
+ * then page p): output page k = i * n_pages + (p - tok_begin / page_tokens)
+ * lands at dev_dst + k * page_bytes, the device layout a page table for
+ * vc_verify_attn then points at.  The call returns once the gather is done and
+ * the copy is enqueued.  No kernel runs.  An unpinned staging buffer is rejected
+ * with VC_ERR_INVALID before any work.
  */
-int vc_prefetch_full_kv(const void* host_pool, void* dev_pool, size_t page_bytes, int n_slots,
-                        const int32_t* page_table, int n_seq_total, int pages_per_seq,
-                        const int32_t* seq_ids, int n_seq, int tok_begin, int tok_end,
-                        int page_tokens, hipStream_t copy_stream, hipEvent_t done);
+int vc_prefetch_full_kv(const void* host_pool, size_t page_bytes, int n_slots, const int32_t* page_table,
+                        int n_seq_total, int pages_per_seq, const int32_t* seq_ids, int n_seq,
+                        int tok_begin, int tok_end, int page_tokens, void* staging, size_t staging_bytes,
+                        void* dev_dst, hipEvent_t staging_free, hipStream_t copy_stream, hipEvent_t done);
 
 #ifdef __cplusplus
 }

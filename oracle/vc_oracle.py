@@ -280,22 +280,18 @@ def accept(draft_ids: np.ndarray, verify_tokens: np.ndarray):
 # ----------------------------------------------------------------------------
 
 
-def prefetch_expected(dev_pool: np.ndarray, host_pool: np.ndarray, page_table: np.ndarray,
-                      seq_ids, tok_begin: int, tok_end: int, page_tokens: int) -> np.ndarray:
-    """Device pool [slots, page_bytes] after copying, for every listed sequence,
-    the pages that hold tokens [tok_begin, tok_end) from the host pool; the page
-    of logical page p of sequence b sits in slot page_table[b, p] in both pools.
-    All other slots keep their bytes."""
-    out = dev_pool.copy()
+def prefetch_expected(host_pool: np.ndarray, page_table: np.ndarray, seq_ids, tok_begin: int, tok_end: int,
+                      page_tokens: int) -> np.ndarray:
+    """Bytes the device receives for one prefetch: for every listed sequence in
+    order, the pages holding tokens [tok_begin, tok_end), each taken from slot
+    page_table[b, p] of the host pool [slots, page_bytes].  Returns
+    [n_seq * n_pages, page_bytes]."""
     if tok_end <= tok_begin:
-        return out
+        return np.zeros((0, host_pool.shape[1]), dtype=host_pool.dtype)
     p0 = tok_begin // page_tokens
     p1 = (tok_end + page_tokens - 1) // page_tokens
-    for b in seq_ids:
-        for p in range(p0, p1):
-            slot = int(page_table[b, p])
-            out[slot] = host_pool[slot]
-    return out
+    rows = [host_pool[int(page_table[b, p])] for b in seq_ids for p in range(p0, p1)]
+    return np.stack(rows)
 
 
 # ----------------------------------------------------------------------------

@@ -305,17 +305,17 @@ def test_accept_pins():
 
 
 def test_prefetch_expected():
+    """Hand-checked gathers: pages come out in (sequence, page) order from the
+    slots the table names; a token range maps to the pages that hold it."""
     host = np.arange(8 * 4, dtype=np.uint8).reshape(8, 4) + 100
-    dev = np.zeros_like(host)
     table = np.array([[3, 0, 6, 1], [2, 7, 4, 5]], dtype=np.int32)
-    out = O.prefetch_expected(dev, host, table, [1], 16, 40, 16)   # pages 1, 2 of seq 1
-    want = np.zeros_like(host)
-    want[7] = host[7]
-    want[4] = host[4]
-    assert np.array_equal(out, want)
-    out = O.prefetch_expected(dev, host, table, [0, 1], 0, 64, 16)
-    assert np.array_equal(out, host)
-    assert np.array_equal(O.prefetch_expected(dev, host, table, [0], 5, 5, 16), dev)
+    out = O.prefetch_expected(host, table, [1], 16, 40, 16)   # tokens 16..39 -> pages 1, 2 of seq 1
+    assert np.array_equal(out, host[[7, 4]])
+    out = O.prefetch_expected(host, table, [1, 0], 0, 64, 16)
+    assert np.array_equal(out, host[[2, 7, 4, 5, 3, 0, 6, 1]])
+    out = O.prefetch_expected(host, table, [0], 17, 18, 16)    # one token -> its page only
+    assert np.array_equal(out, host[[0]])
+    assert O.prefetch_expected(host, table, [0], 5, 5, 16).shape == (0, 4)
 
 
 # ------------------------------------------------------------ whole round ---

@@ -244,17 +244,74 @@ def test_prefetch_pages_bit_exact():
     page_bytes, slots, nseq, pps, pt = 4096, 64, 4, 16, 16
     rng = np.random.default_rng(3)
     table = rng.permutation(slots).astype(np.int32).reshape(nseq, pps)
-    host = torch.empty(slots * page_bytes, dtype=torch.uint8, pin_memory=True)
-    host.copy_(torch.from_numpy(rng.integers(0, 256, slots * page_bytes, dtype=np.uint8)))
-    dev0 = rng.integers(0, 256, slots * page_bytes, dtype=np.uint8)
-    dev = torch.from_numpy(dev0).cuda()
+    host = torch.from_numpy(rng.integers(0, 256, slots * page_bytes, dtype=np.uint8))
+    staging = torch.empty(slots * page_bytes, dtype=torch.uint8, pin_memory=True)
+    dev = torch.full((slots * page_bytes,), 7, dtype=torch.uint8, device="cuda")
     s = torch.cuda.Stream()
-    vc.prefetch_full_kv(host, dev, page_bytes, table, [1, 3], 40, 200, pt, stream=s)
-    s.synchronize()
-    want = O.prefetch_expected(dev0.reshape(slots, page_bytes), host.numpy().reshape(slots, page_bytes),
-                               table, [1, 3], 40, 200, pt)
-    assert np.array_equal(dev.cpu().numpy().reshape(slots, page_bytes), want)
-    # unpinned host memory is rejected before anything is enqueued
+    done = torch.cuda.Event()
+    for (seqs, t0, t1) in [([1, 3], 40, 200), ([2], 0, 256), ([0, 1, 2, 3], 17, 18)]:
+        vc.prefetch_full_kv(host, page_bytes, table, seqs, t0, t1, pt, staging, dev, stream=s, done_event=done)
+        s.synchronize()
+        want = O.prefetch_expected(host.numpy().reshape(slots, page_bytes), table, seqs, t0, t1, pt)
+        got = dev.cpu().numpy()[:want.size].reshape(want.shape)
+        assert np.array_equal(got, want), (seqs, t0, t1)
+    # an unpinned staging buffer is rejected before any work
     with pytest.raises(vc.VcError):
-        vc.prefetch_full_kv(torch.empty(slots * page_bytes, dtype=torch.uint8), dev, page_bytes, table, [0],
-                            0, 16, pt, stream=s)
+        vc.prefetch_full_kv(host, page_bytes, table, [0], 0, 16, pt, torch.empty(page_bytes, dtype=torch.uint8),
+                            dev, stream=s)
+
+
+def test_prefetched_pages_feed_paged_verify():
+    """Full-KV chunks of a shuffled host pool, prefetched chunk by chunk, then read
+    through a device page table by the paged verify kernel: equals the oracle."""
+    import torch
+    vc = _vc()
+    from compressed_kv_draft_amd.workload import bf16_dev, paged_pool
+    print("[case] prefetch -> paged verify", flush=True)
+    w = C.TINY.with_(name="pv", B=2, Hq=8, Hkv=2, D=64, L=512, k=7, kind="identity", paged=True, page_tokens=16,
+                     chunk_tokens=128, seed=61)
+    K, V = I.context_kv(w, "k"), I.context_kv(w, "v")
+    Kn, Vn = I.new_rows(w, "k"), I.new_rows(w, "v")
+    Q = I.queries(w)
+    table, n_slots = I.page_table(w)
+    pool = paged_pool(w, np.concatenate([K, Kn], 2), np.concatenate([V, Vn], 2), table, n_slots)
+    page_bytes = pool[0].nbytes
+    host = torch.from_numpy(pool.reshape(-1).view(np.uint8).copy())
+    ctx_pages = w.L // w.page_tokens
+    pps = table.shape[1]
+    # device region: chunk c of all sequences, then the pages of the new rows
+    per_chunk = w.chunk_tokens // w.page_tokens
+    dev = torch.empty((w.B * pps + 1) * page_bytes, dtype=torch.uint8, device="cuda")
+    dev_table = np.zeros_like(table)
+    staging = [torch.empty(w.B * per_chunk * page_bytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+    done = [torch.cuda.Event(), torch.cuda.Event()]
+    s = torch.cuda.Stream()
+    base = 0
+    for c, t0 in enumerate(range(0, w.L, w.chunk_tokens)):
+        seqs = list(range(w.B))
+        vc.prefetch_full_kv(host, page_bytes, table, seqs, t0, t0 + w.chunk_tokens, w.page_tokens, staging[c % 2],
+                            dev[base * page_bytes:], stream=s, done_event=done[c % 2],
+                            staging_free=done[c % 2] if c >= 2 else None)
+        for i, b in enumerate(seqs):
+            dev_table[b, t0 // w.page_tokens:(t0 + w.chunk_tokens) // w.page_tokens] = \
+                base + i * per_chunk + np.arange(per_chunk)
+        base += w.B * per_chunk
+    # the pages holding the drafted rows live only on the device
+    for b in range(w.B):
+        for p in range(ctx_pages, pps):
+            dev[base * page_bytes:(base + 1) * page_bytes].copy_(
+                torch.from_numpy(pool[table[b, p]].reshape(-1).view(np.uint8).copy()))
+            dev_table[b, p] = base
+            base += 1
+    s.synchronize()
+    torch.cuda.synchronize()
+    pool_dev = dev.view(torch.bfloat16)
+    tab_dev = torch.from_numpy(dev_table).cuda()
+    full = vc.FullKV(pool_dev, None, 0, tab_dev, w.page_tokens, pps, base)
+    ctx = torch.full((w.B,), w.L, dtype=torch.int32, device="cuda")
+    got = vc.verify_attn(bf16_dev(Q, "cuda"), full, ctx, w.L, w.Hkv, O.scale_for(w.D)).cpu().numpy()
+    g = w.g
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            ref = R.unit_verify(w, K[b, h], V[b, h], Kn[b, h], Vn[b, h], Q[b, h * g:(h + 1) * g])
+            assert_close(got[b, h * g:(h + 1) * g], ref, f"prefetched paged verify b{b} h{h}")
