@@ -8,8 +8,9 @@
 // multiply-adds per HBM byte, more than fp32 vector ALUs sustain at HBM speed,
 // so both products run on the f16 matrix cores, exactly:
 //  * a code c placed in the mantissa of an f16 bit pattern is the subnormal
-//    c * 2^(bits*jj - 24) (jj = its position in the byte) -- one AND turns two
-//    packed codes into two exact f16 operands;
+//    c * 2^(bits*jj - 24) (jj = its position in the byte) -- a shift and an AND
+//    turn two packed codes into two exact f16 operands (always at one of the
+//    byte's two highest positions, see code_target);
 //  * K is grouped per channel, so its scale goes into the query: q_h * s is
 //    computed in f16 as hi + lo (a rounded product and its exact residual, one
 //    fma), giving 22 significand bits; hi and lo are adjacent MFMA columns;
@@ -87,13 +88,26 @@ struct Cfg {
   static constexpr int SMEM = kWaves * STAGE_BYTES > EPI_BYTES ? kWaves * STAGE_BYTES : EPI_BYTES;
 };
 
-// Two packed codes (bits b and b+16 of w, position j of the dword) as an f16 pair:
-// code * 2^(bits * (j % PER) - 24) each, exactly.
+// Position inside its byte at which code pair j of a dword is handed to the
+// matrix cores: always one of the two highest (int2: 2 or 3, int4: 1).  The f16
+// products sum with a truncating internal alignment when their magnitudes
+// differ widely; keeping the code operands at least 2^(4-24) avoids the large
+// systematic bias the lowest subnormals (2^-24) showed on the device.
+template <int BITS>
+__host__ __device__ constexpr int code_target(int j) {
+  return BITS == 4 ? 1 : 2 + ((j % (8 / BITS)) & 1);
+}
+
+// Two packed codes (bits b and b+16 of w, pair position j of the dword) as an
+// f16 pair: code * 2^(bits * code_target(j) - 24) each, exactly.
 template <int BITS>
 __device__ __forceinline__ uint32_t code_pair(uint32_t w, int j) {
   constexpr int PER = 8 / BITS;
   constexpr uint32_t MASK = BITS == 2 ? 0x00030003u : 0x000F000Fu;
-  return (w >> (8 * (j / PER))) & (MASK << (BITS * (j % PER)));
+  const int jt = code_target<BITS>(j);
+  const int sh = 8 * (j / PER) + BITS * (j % PER) - BITS * jt;
+  const uint32_t ws = sh >= 0 ? (w >> sh) : (w << -sh);
+  return ws & (MASK << (BITS * jt));
 }
 
 // N consecutive dwords from an address aligned to min(16, 4N) bytes.
@@ -328,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void draft_mfma_kernel(DraftArgs a) {
             const int pi = 4 * ks + i, d = pi / C::PPD, j = pi % C::PPD;
             const int ca = C::CPD * d + j, cb = ca + C::CPD / 2;
             const float xa = bf16_to_f32(qh[ca]), xb = bf16_to_f32(qh[cb]);
-            const float f = __builtin_ldexpf(1.0f, kQExp - BITS * (j % C::PER));
+            const float f = __builtin_ldexpf(1.0f, kQExp - BITS * code_target<BITS>(j));
             const f16x2 pf = {(_Float16)(xa * f), (_Float16)(xb * f)};
             const f16x2 pz = {(_Float16)xa, (_Float16)xb};
             qF[ks][i] = __builtin_bit_cast(uint32_t, pf);
@@ -464,8 +478,8 @@ __global__ __launch_bounds__(kThreads) void draft_mfma_kernel(DraftArgs a) {
             const float x0 = P[2 * k] * f16lo(mm[2 * k]), x1 = P[2 * k + 1] * f16lo(mm[2 * k + 1]);
             zs = fmaf(P[2 * k], f16hi(mm[2 * k]), zs);
             zs = fmaf(P[2 * k + 1], f16hi(mm[2 * k + 1]), zs);
-            const auto h = __builtin_amdgcn_cvt_pkrtz(x0, x1);  // truncated hi; x - hi is exact
-            const auto l = __builtin_amdgcn_cvt_pkrtz(x0 - (float)h[0], x1 - (float)h[1]);
+            const f16x2 h = {(_Float16)x0, (_Float16)x1};  // nearest-even hi; x - hi is exact
+            const f16x2 l = {(_Float16)(x0 - (float)h[0]), (_Float16)(x1 - (float)h[1])};
             hi4[k] = __builtin_bit_cast(uint32_t, h);
             lo4[k] = __builtin_bit_cast(uint32_t, l);
           }
@@ -555,7 +569,7 @@ __global__ __launch_bounds__(kThreads) void draft_mfma_kernel(DraftArgs a) {
   for (int ct = 0; ct < NCT; ++ct) {
     if (quant_wg) {
       constexpr int B2 = BITS > 0 ? BITS : 2;
-      const float osc = __builtin_ldexpf(1.0f, 24 - B2 * ((ct % Cfg<D, B2>::PPD) % Cfg<D, B2>::PER));
+      const float osc = __builtin_ldexpf(1.0f, 24 - B2 * code_target<B2>(ct % Cfg<D, B2>::PPD));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * quad + i;
