@@ -123,8 +123,8 @@ def quantize_kv(k_src: torch.Tensor, v_src: torch.Tensor, bits: int, n_quant: in
     t = dict(bits=bits, n_quant=n_quant,
              k_codes=torch.empty((B, Hkv, n_quant, rb), dtype=torch.uint8, device=dev),
              v_codes=torch.empty((B, Hkv, n_quant, rb), dtype=torch.uint8, device=dev),
-             k_meta=torch.empty((B, Hkv, n_quant // 32, D, 2), dtype=torch.float16, device=dev),
-             v_meta=torch.empty((B, Hkv, n_quant, D // 32, 2), dtype=torch.float16, device=dev))
+             k_meta=torch.empty((B, Hkv, n_quant // 32, 2, D), dtype=torch.float16, device=dev),
+             v_meta=torch.empty((B, Hkv, n_quant // 32, D // 32, 32, 2), dtype=torch.float16, device=dev))
     comp = Compressed("quant", **t)
     rc = LIB.vc_quantize_kv(_ptr(k_src), _ptr(v_src), B, Hkv, L_cap, D, ctypes.byref(comp.desc), _stream(stream))
     _check(rc, "vc_quantize_kv")

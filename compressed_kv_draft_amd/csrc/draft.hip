@@ -68,6 +68,58 @@ constexpr int kThreads = 64 * kWaves;
 constexpr float kTau = 8.0f;  // lazy rescale: the running max moves only when exceeded by 2^8
 constexpr int kQExp = 4;      // q is scaled by 2^kQExp before it multiplies the K scales
 
+constexpr int cmax(int x, int y) { return x > y ? x : y; }
+constexpr int cmin(int x, int y) { return x < y ? x : y; }
+constexpr int kLdsPerCu = 160 * 1024;
+
+// Direct global -> LDS copies: each load instruction moves 16 bytes per lane,
+// lane i's to LDS byte 16 i of its 1 KiB (gfx950 global_load_lds_dwordx4, LDS
+// base address in M0).  Issued from inline assembly so that the compiler does
+// not see them: it would otherwise wait for every outstanding one (vmcnt(0))
+// before any LDS read it cannot prove disjoint, which defeats the prefetch.
+// M0 is saved and restored around the load.
+constexpr int lds_dma_count(int bytes) { return (bytes + 1023) / 1024; }
+
+__device__ __forceinline__ void lds_dma16(const unsigned char* base, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(base), "s"(lds_addr)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  using lptr = __attribute__((address_space(3))) const void*;
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lptr)p);
+}
+
+// BYTES from the wave-uniform address gbase to the wave-uniform LDS address lds;
+// voff = 16 * lane.
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(const unsigned char* gbase, uint32_t voff, uint32_t lds, int lane) {
+  static_assert(BYTES % 16 == 0, "");
+#pragma unroll
+  for (int k = 0; k < BYTES / 1024; ++k) lds_dma16(gbase + 1024 * k, voff, lds + 1024 * k);
+  if constexpr (BYTES % 1024 != 0) {
+    constexpr int k = BYTES / 1024;
+    if (lane < (BYTES % 1024) / 16) lds_dma16(gbase + 1024 * k, voff, lds + 1024 * k);
+  }
+}
+
+// Waits for those loads are explicit.  Loads complete in order, so "at most N outstanding" means all but the last N
+// load instructions have written LDS.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 template <int D, int BITS>
 struct Cfg {
   static constexpr int NKS = D / 32;   // k-steps of q.k
@@ -82,10 +134,32 @@ struct Cfg {
   static constexpr int VDW = D * B_ / 64;   // V code dwords per lane per block
   static constexpr int VMD = NG / 2;        // V meta dwords staged per lane per block
   static constexpr int VPITCH = D + 16;     // LDS row pitch (elements) of staged bf16 V
-  static constexpr int META_DW = BITS > 0 ? 2 * 16 * NKS + 32 * NG + 8 : 0;  // + 8 zero dwords
-  static constexpr int STAGE_BYTES = META_DW * 4 + 32 * VPITCH * 2;
+  static constexpr int ROWS_WAVE = 32 * VPITCH * 2;  // per-wavefront LDS of the exact-row path
+  // one 32-token block of the compressed streams (all multiples of 16 bytes)
+  static constexpr int ROW_BYTES = D * B_ / 8;  // K codes of one token
+  static constexpr int KC_BYTES = 32 * ROW_BYTES;
+  static constexpr int VC_BYTES = 32 * ROW_BYTES;
+  static constexpr int KM_BYTES = 4 * D;  // scale plane + zero plane, f16, pair order
+  static constexpr int VM_BYTES = 4 * D;  // [NG][32 tokens] {scale, zero}
+  static constexpr int VC_OFF = KC_BYTES, KM_OFF = VC_OFF + VC_BYTES, VM_OFF = KM_OFF + KM_BYTES;
+  static constexpr int SLOT = VM_OFF + VM_BYTES;
+  static constexpr int NDMA = lds_dma_count(KC_BYTES) + lds_dma_count(VC_BYTES) + lds_dma_count(KM_BYTES) +
+                              lds_dma_count(VM_BYTES);  // load instructions per block
+  // shared by the workgroup's wavefronts: zeros, and (int2) the query as f16
+  static constexpr int ZERO_BYTES = 64 * NKS;
+  static constexpr int QZ_BYTES = BITS == 2 ? 8 * 4 * NKS * 16 : 0;  // [head][quad][ks] u32x4
+  static constexpr int SHARED_BYTES = BITS == 0 ? 0 : ZERO_BYTES + QZ_BYTES;
+  // ring slots per wavefront: up to 4; as many as leave room for 4 workgroups
+  // per CU if that gives at least 2, else for 3
+  static constexpr int D4 = (kLdsPerCu / 4 - SHARED_BYTES) / kWaves / SLOT;
+  static constexpr int D3 = (kLdsPerCu / 3 - SHARED_BYTES) / kWaves / SLOT;
+  static constexpr int DEPTH = BITS == 0 ? 0 : cmin(4, D4 >= 2 ? D4 : D3);
+  static constexpr int RING_WAVE = DEPTH * SLOT;
+  static constexpr int ZERO_OFF = kWaves * RING_WAVE, QZ_OFF = ZERO_OFF + ZERO_BYTES;
   static constexpr int EPI_BYTES = kWaves * (8 * D + 8 + 8 + 8 * 4) * 4;
-  static constexpr int SMEM = kWaves * STAGE_BYTES > EPI_BYTES ? kWaves * STAGE_BYTES : EPI_BYTES;
+  static constexpr int SMEM = cmax(cmax(kWaves * RING_WAVE + SHARED_BYTES, kWaves * ROWS_WAVE), EPI_BYTES);
+  // wavefronts per SIMD the register allocation aims at: as many as LDS allows, up to 4
+  static constexpr int WAVES = cmin(4, kLdsPerCu / SMEM);
 };
 
 // Position inside its byte at which code pair j of a dword is handed to the
@@ -281,7 +355,8 @@ __device__ __forceinline__ void rows_block(const RowSrc& src, int blk, const bf1
 }
 
 template <int D, int BITS, int NV>
-__global__ __launch_bounds__(kThreads) void draft_mfma_kernel(DraftArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D, BITS>::WAVES))) void draft_mfma_kernel(
+    DraftArgs a) {
   using C = Cfg<D, BITS>;
   constexpr int NKS = C::NKS, NCT = C::NCT, NG = C::NG;
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM];
@@ -299,11 +374,7 @@ __global__ __launch_bounds__(kThreads) void draft_mfma_kernel(DraftArgs a) {
   const int slot = 2 * rep + hilo;
   const bool slot_ok = rep < R8;
 
-  unsigned char* stage = smem + wave * C::STAGE_BYTES;
-  uint32_t* sp = reinterpret_cast<uint32_t*>(stage);  // [4 quads][NKS][4] K-scale pairs
-  uint32_t* zp = sp + 16 * NKS;                       // [4][NKS][4] K-zero pairs
-  uint32_t* vm = zp + 16 * NKS;                       // [NG][4 quads][8 slots] V {scale, zero}
-  uint16_t* vst = reinterpret_cast<uint16_t*>(stage + C::META_DW * 4);
+  uint16_t* vst = reinterpret_cast<uint16_t*>(smem + wave * C::ROWS_WAVE);  // exact-row path
 
   // this lane's query head, channels quad * D/4 .. + D/4
   const uint16_t* qrow = a.q + ((size_t)b * a.Hq + hk * g + head) * D + quad * (D / 4);
@@ -331,12 +402,17 @@ __global__ __launch_bounds__(kThreads) void draft_mfma_kernel(DraftArgs a) {
     const int bhi = min(blo + a.main_bpw, nb);
     if constexpr (BITS > 0) {
       // ---------------------------------------------------------------- quant
-      // q scaled per k slot (f16, exact): qF = q 2^(kQExp - bits*jj); qz = q
-      uint32_t qF[NKS][4], qz[NKS][4];
+      // q scaled per k slot (f16, exact): qF = q 2^(kQExp - bits*jj).  The zero-
+      // point product needs q itself: for int4 that is qF (jj is 1), for int2
+      // it comes from a workgroup table in LDS.
+      uint32_t qF[NKS][4];
+      uint32_t* zero = reinterpret_cast<uint32_t*>(smem + C::ZERO_OFF);
+      uint32_t* qzt = reinterpret_cast<uint32_t*>(smem + C::QZ_OFF);  // [head][quad][ks][4]
       {
         const uint16_t* qh = reinterpret_cast<const uint16_t*>(qraw);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
+          u32x4 z4;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int pi = 4 * ks + i, d = pi / C::PPD, j = pi % C::PPD;
@@ -346,93 +422,88 @@ __global__ __launch_bounds__(kThreads) void draft_mfma_kernel(DraftArgs a) {
             const f16x2 pf = {(_Float16)(xa * f), (_Float16)(xb * f)};
             const f16x2 pz = {(_Float16)xa, (_Float16)xb};
             qF[ks][i] = __builtin_bit_cast(uint32_t, pf);
-            qz[ks][i] = __builtin_bit_cast(uint32_t, pz);
+            z4[i] = __builtin_bit_cast(uint32_t, pz);
           }
+          if (BITS == 2 && wave == 0 && rep == 0 && hilo == 0)
+            *reinterpret_cast<u32x4*>(qzt + ((head * 4 + quad) * NKS + ks) * 4) = z4;
         }
       }
-      // qFm = qF in lo columns, 0 in hi columns
-      uint32_t qFm[NKS][4];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) qFm[ks][i] = hilo ? qF[ks][i] : 0u;
-      // K-meta pair this lane stages: (quad', ks', i') = lane
+      for (int i = threadIdx.x; i < C::ZERO_BYTES / 4; i += kThreads) zero[i] = 0u;
+      __syncthreads();
+
+      // This wavefront's blocks stream through a ring of DEPTH LDS slots filled
+      // by direct global->LDS loads, DEPTH-1 blocks ahead of the block in use:
+      // no registers hold data in flight, and the metadata arrive already in
+      // the order the matrix-core operands read them.  All addressing of the
+      // loads is wave-uniform (scalar registers) plus the lane's 16-byte offset.
       const int nq32 = a.n_quant / 32;
-      int kma = 0, kmb = 0;
-      const bool kstage = lane < 16 * NKS;
-      {
-        const int q_ = lane / (4 * NKS), ks_ = (lane / 4) % NKS, i_ = lane % 4;
-        const int pi = 4 * ks_ + i_, d = pi / C::PPD, j = pi % C::PPD;
-        kma = q_ * (D / 4) + C::CPD * d + j;
-        kmb = kma + C::CPD / 2;
-      }
-      const uint8_t* kcodes = a.k_codes + unit_rows * a.n_quant * (D * BITS / 8) + quad * (D * BITS / 32);
-      const uint8_t* vcodes = a.v_codes + unit_rows * a.n_quant * (D * BITS / 8) + lane * (C::VDW * 4);
-      const uint32_t* kmeta = a.k_meta + unit_rows * nq32 * D;
-      const uint32_t* vmeta = a.v_meta + unit_rows * a.n_quant * NG + lane * C::VMD;
-
-      struct Raw {
-        uint32_t kc[2][C::KDW];
-        uint32_t vc[C::VDW];
-        uint32_t km[2];
-        uint32_t vmt[C::VMD];
+      const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+      const unsigned char* kcodes = a.k_codes + unit_rows * nq32 * C::KC_BYTES;
+      const unsigned char* vcodes = a.v_codes + unit_rows * nq32 * C::VC_BYTES;
+      const unsigned char* kmeta = reinterpret_cast<const unsigned char*>(a.k_meta) + unit_rows * nq32 * C::KM_BYTES;
+      const unsigned char* vmeta = reinterpret_cast<const unsigned char*>(a.v_meta) + unit_rows * nq32 * C::VM_BYTES;
+      const unsigned char* ring = smem + wave * C::RING_WAVE;
+      const uint32_t ring_lds = lds_address(smem) + wave_u * C::RING_WAVE;
+      const uint32_t voff = 16 * lane;
+      const int first = blo + wave_u;
+      const int nw = first < bhi ? (bhi - first + kWaves - 1) / kWaves : 0;  // blocks of this wavefront
+      auto issue = [&](int k) {
+        const size_t blk = (size_t)(first + kWaves * k);
+        const uint32_t sl = ring_lds + (k % C::DEPTH) * C::SLOT;
+        lds_dma<C::KC_BYTES>(kcodes + blk * C::KC_BYTES, voff, sl, lane);
+        lds_dma<C::VC_BYTES>(vcodes + blk * C::VC_BYTES, voff, sl + C::VC_OFF, lane);
+        lds_dma<C::KM_BYTES>(kmeta + blk * C::KM_BYTES, voff, sl + C::KM_OFF, lane);
+        lds_dma<C::VM_BYTES>(vmeta + blk * C::VM_BYTES, voff, sl + C::VM_OFF, lane);
       };
-      auto load = [&](int blk, Raw& r) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const uint8_t* p = kcodes + (size_t)(32 * blk + 16 * tt + col) * (D * BITS / 8);
-          load_dwords<C::KDW>(p, r.kc[tt]);
-        }
-        load_dwords<C::VDW>(vcodes + (size_t)blk * 64 * (C::VDW * 4), r.vc);
-        if (kstage) {
-          r.km[0] = kmeta[(size_t)blk * D + kma];
-          r.km[1] = kmeta[(size_t)blk * D + kmb];
-        } else {
-          r.km[0] = r.km[1] = 0u;
-        }
-#pragma unroll
-        for (int u = 0; u < C::VMD; ++u) r.vmt[u] = vmeta[(size_t)blk * 32 * NG + u];
-      };
+      for (int k = 0; k < C::DEPTH - 1; ++k)
+        if (k < nw) issue(k);
+      // operand of the rounded product q~hi = qF s: the block's scales in the lo
+      // columns, zeros in the hi columns (whose q~ is then RN(qF s) itself)
+      const int tsel = hilo ? 1 : 0;
 
-      // lanes whose column has no V group read 8 zero dwords instead
-      if (lane < 8) vm[32 * NG + lane] = 0u;
-      int blk = blo + wave;
-      Raw cur;
-      if (blk < bhi) load(blk, cur);
-      while (blk < bhi) {
-        // stage this block's meta in LDS (wavefront-private region; LDS ops of one
-        // wavefront complete in order, so the reads below see these writes)
-        if (kstage) {
-          sp[lane] = (cur.km[0] & 0xFFFFu) | (cur.km[1] << 16);
-          zp[lane] = (cur.km[0] >> 16) | (cur.km[1] & 0xFFFF0000u);
+      for (int k = 0; k < nw; ++k) {
+        if (k + C::DEPTH - 1 < nw) {
+          wait_lds_reads();  // the slot being refilled was last read in the previous iteration
+          issue(k + C::DEPTH - 1);
         }
-#pragma unroll
-        for (int u = 0; u < C::VMD; ++u) {
-          const int d = lane * C::VMD + u, t = d / NG, G = d % NG;
-          vm[(G * 4 + (t % 16) / 4) * 8 + (t % 4) + 4 * (t / 16)] = cur.vmt[u];
-        }
-        const int nxt = blk + kWaves;
-        Raw nx;
-        if (nxt < bhi) load(nxt, nx);
+        // block k has landed once at most the loads of the blocks after it are outstanding
+        const int ahead = min(nw - 1 - k, C::DEPTH - 1);
+        if (ahead >= 3) wait_vmem<3 * C::NDMA>();
+        else if (ahead == 2) wait_vmem<2 * C::NDMA>();
+        else if (ahead == 1) wait_vmem<C::NDMA>();
+        else wait_vmem<0>();
+        const unsigned char* sl = ring + (k % C::DEPTH) * C::SLOT;
+        const uint32_t* sp = reinterpret_cast<const uint32_t*>(sl + C::KM_OFF);  // [4 quads][NKS][4] scale pairs
+        const uint32_t* zp = sp + 16 * NKS;                                     // [4][NKS][4] zero pairs
+        const uint32_t* vm = reinterpret_cast<const uint32_t*>(sl + C::VM_OFF);  // [NG][4 quads][8] {scale, zero}
+        const uint32_t* tp = tsel ? sp : zero;
 
         // q~ = hi or lo part of qF * s_K, and the K zero-point product z . q
         f32x4 accZ = {0.f, 0.f, 0.f, 0.f};
         f16x8 qt[NKS];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-          const u32x4 z4 = *reinterpret_cast<const u32x4*>(zp + (quad * NKS + ks) * 4);
-          const u32x4 qz4 = {qz[ks][0], qz[ks][1], qz[ks][2], qz[ks][3]};
+          const int o = (quad * NKS + ks) * 4;
+          const u32x4 z4 = *reinterpret_cast<const u32x4*>(zp + o);
+          u32x4 qz4;
+          if constexpr (BITS == 4) {
+            qz4 = u32x4{qF[ks][0], qF[ks][1], qF[ks][2], qF[ks][3]};
+          } else {
+            qz4 = *reinterpret_cast<const u32x4*>(qzt + ((head * 4 + quad) * NKS + ks) * 4);
+          }
           accZ = mfma_f16(__builtin_bit_cast(f16x8, z4), __builtin_bit_cast(f16x8, qz4), accZ);
-          const u32x4 s4 = *reinterpret_cast<const u32x4*>(sp + (quad * NKS + ks) * 4);
+          const u32x4 s4 = *reinterpret_cast<const u32x4*>(sp + o);
+          const u32x4 t4 = *reinterpret_cast<const u32x4*>(tp + o);
           u32x4 r4;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             // (bit-casting the subscript s4[i] directly reads element 0: copy it out first)
-            const uint32_t sw = s4[i];
-            const f16x2 s = __builtin_bit_cast(f16x2, sw);
+            const uint32_t sw = s4[i], tw = t4[i];
+            const f16x2 sv = __builtin_bit_cast(f16x2, sw);
             const f16x2 qf = __builtin_bit_cast(f16x2, qF[ks][i]);
-            const f16x2 t = __builtin_bit_cast(f16x2, qFm[ks][i]) * s;  // RN(qF s) or 0
-            r4[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qf, s, -t));  // hi or lo
+            const f16x2 t = qf * __builtin_bit_cast(f16x2, tw);  // RN(qF s) or 0
+            r4[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qf, sv, -t));  // hi or lo
           }
           qt[ks] = __builtin_bit_cast(f16x8, r4);
         }
@@ -442,6 +513,8 @@ __global__ __launch_bounds__(kThreads) void draft_mfma_kernel(DraftArgs a) {
         float x[8];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
+          uint32_t kw[C::KDW];
+          load_dwords<C::KDW>(sl + (16 * tt + col) * C::ROW_BYTES + quad * (C::ROW_BYTES / 4), kw);
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) {
@@ -449,7 +522,7 @@ __global__ __launch_bounds__(kThreads) void draft_mfma_kernel(DraftArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int pi = 4 * ks + i;
-              a4[i] = code_pair<BITS>(cur.kc[tt][pi / C::PPD], pi % C::PPD);
+              a4[i] = code_pair<BITS>(kw[pi / C::PPD], pi % C::PPD);
             }
             acc = mfma_f16(__builtin_bit_cast(f16x8, a4), qt[ks], acc);
           }
@@ -461,33 +534,34 @@ __global__ __launch_bounds__(kThreads) void draft_mfma_kernel(DraftArgs a) {
         }
         float P[8];
         softmax_block<NCT, NV>(x, st, P, quad);
-        // A operands: hi and lo of P * s_V for this lane's channel group(s)
+        // A operands: hi and lo of P * s_V for this lane's channel group(s);
+        // hi = RN_f16(P s), lo = RN_f16(P s - hi), each one mixed-precision fma
         f16x8 Ahi[NV], Alo[NV];
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
           const int G = slot + v * SP;
           const bool gok = slot_ok && G < NG;
-          const uint32_t* vmg = vm + (gok ? (G * 4 + quad) * 8 : 32 * NG);
+          const uint32_t* vmg = gok ? vm + (G * 4 + quad) * 8 : zero;
           const u32x4 m0 = *reinterpret_cast<const u32x4*>(vmg);
           const u32x4 m1 = *reinterpret_cast<const u32x4*>(vmg + 4);
           const uint32_t mm[8] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
           float zs = 0.0f;
-          u32x4 hi4, lo4;
+          _Float16 hv[8], lv[8];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float x0 = P[2 * k] * f16lo(mm[2 * k]), x1 = P[2 * k + 1] * f16lo(mm[2 * k + 1]);
-            zs = fmaf(P[2 * k], f16hi(mm[2 * k]), zs);
-            zs = fmaf(P[2 * k + 1], f16hi(mm[2 * k + 1]), zs);
-            const f16x2 h = {(_Float16)x0, (_Float16)x1};  // nearest-even hi; x - hi is exact
-            const f16x2 l = {(_Float16)(x0 - (float)h[0]), (_Float16)(x1 - (float)h[1])};
-            hi4[k] = __builtin_bit_cast(uint32_t, h);
-            lo4[k] = __builtin_bit_cast(uint32_t, l);
+          for (int e = 0; e < 8; ++e) {
+            const f16x2 sz = __builtin_bit_cast(f16x2, mm[e]);
+            const float sc = (float)sz[0];
+            hv[e] = (_Float16)fmaf(P[e], sc, 0.0f);
+            lv[e] = (_Float16)fmaf(P[e], sc, -(float)hv[e]);
+            zs = fmaf(P[e], (float)sz[1], zs);
           }
-          Ahi[v] = __builtin_bit_cast(f16x8, hi4);
-          Alo[v] = __builtin_bit_cast(f16x8, lo4);
+          Ahi[v] = f16x8{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]};
+          Alo[v] = f16x8{lv[0], lv[1], lv[2], lv[3], lv[4], lv[5], lv[6], lv[7]};
           st.zacc[v] += zs;
         }
         // P.V code part
+        uint32_t vw[C::VDW];
+        load_dwords<C::VDW>(sl + C::VC_OFF + lane * (C::VDW * 4), vw);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           const int v = NV == 1 ? 0 : ct / 4;
@@ -495,13 +569,11 @@ __global__ __launch_bounds__(kThreads) void draft_mfma_kernel(DraftArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int pi = i * NCT + ct;
-            b4[i] = code_pair<BITS>(cur.vc[pi / C::PPD], pi % C::PPD);
+            b4[i] = code_pair<BITS>(vw[pi / C::PPD], pi % C::PPD);
           }
           st.O[ct] = mfma_f16(Ahi[v], __builtin_bit_cast(f16x8, b4), st.O[ct]);
           st.O[ct] = mfma_f16(Alo[v], __builtin_bit_cast(f16x8, b4), st.O[ct]);
         }
-        cur = nx;
-        blk = nxt;
       }
     } else {
       // ---------------------------------------------------- exact rows (main)
@@ -672,12 +744,15 @@ struct DraftPlan {
 
 constexpr int kTailBpw = 2 * kWaves;  // tail workgroups: up to 2 blocks per wavefront
 
-// wgs_per_cu: resident workgroups per CU of the kernel that will run; the main
-// part is sized to fill the chip exactly once.
+// wgs_per_cu: resident workgroups per CU of the kernel that will run.  The
+// tail workgroups are placed first; the main part takes the remaining resident
+// slots, so that every workgroup of the grid starts at once.
 DraftPlan plan_draft(int units, int main_blocks, int tail_blocks, int wgs_per_cu) {
   DraftPlan p{};
+  p.tail_bpw = kTailBpw;
+  p.tail_splits = (tail_blocks + kTailBpw - 1) / kTailBpw;
   if (main_blocks > 0) {
-    const int target = wgs_per_cu * num_cus();
+    const int target = wgs_per_cu * num_cus() - units * p.tail_splits;
     int s = target / units;
     const int cap = (main_blocks + 2 * kWaves - 1) / (2 * kWaves);  // >= 2 blocks per wavefront
     if (s > cap) s = cap;
@@ -685,8 +760,6 @@ DraftPlan plan_draft(int units, int main_blocks, int tail_blocks, int wgs_per_cu
     p.main_bpw = (main_blocks + s - 1) / s;
     p.main_splits = (main_blocks + p.main_bpw - 1) / p.main_bpw;
   }
-  p.tail_bpw = kTailBpw;
-  p.tail_splits = (tail_blocks + kTailBpw - 1) / kTailBpw;
   p.splits = p.main_splits + p.tail_splits;
   if (p.splits == 0) {  // no key at all: one empty workgroup writes o = 0
     p.tail_splits = 1;
@@ -760,9 +833,9 @@ extern "C" int vc_draft_attn(const vc_kv_comp* comp, const vc_tail* tail, const 
                comp->n_quant);
       VC_CHECK(comp->n_quant == 0 || (comp->k_codes && comp->v_codes && comp->k_meta && comp->v_meta),
                "vc_draft_attn: null codes/meta");
-      VC_CHECK(aligned(comp->k_codes, 16) && aligned(comp->v_codes, 16) && aligned(comp->k_meta, 4) &&
-                   aligned(comp->v_meta, 8),
-               "vc_draft_attn: codes must be 16-byte, K meta 4-byte and V meta 8-byte aligned");
+      VC_CHECK(aligned(comp->k_codes, 16) && aligned(comp->v_codes, 16) && aligned(comp->k_meta, 16) &&
+                   aligned(comp->v_meta, 16),
+               "vc_draft_attn: codes and meta must be 16-byte aligned");
       bits = comp->bits;
       a.n_quant = comp->n_quant;
       a.n_main = comp->n_quant;

@@ -65,10 +65,10 @@ __global__ void quant_k_kernel(const uint16_t* __restrict__ src, int L_cap, int 
     const float s = (float)sh, z = (float)zh;
 #pragma unroll
     for (int i = 0; i < 32; ++i) packed[i] |= code_of(x[i], s, z, QMAX) << (BITS * e);
-    H2 m;
-    m.s = sh;
-    m.z = zh;
-    meta[((size_t)unit * (n_quant / 32) + blk) * D + d] = m;
+    _Float16* plane = reinterpret_cast<_Float16*>(meta + ((size_t)unit * (n_quant / 32) + blk) * D);
+    const int pos = kmeta_pos(D, BITS, d);
+    plane[pos] = sh;
+    plane[D + pos] = zh;
   }
   uint8_t* out = codes + ((size_t)unit * n_quant + (size_t)blk * 32) * row_bytes + col;
 #pragma unroll
@@ -96,7 +96,7 @@ __global__ void quant_v_meta_kernel(const uint16_t* __restrict__ src, int L_cap,
   }
   H2 m;
   group_params(mn, mx, QMAX, m.s, m.z);
-  meta[((size_t)unit * n_quant + t) * G + grp] = m;
+  meta[(((size_t)unit * (n_quant / 32) + t / 32) * G + grp) * 32 + vmeta_slot(t % 32)] = m;
 }
 
 // V pass 2, one thread per code byte of the tiled layout (vc_vcode_locate in
@@ -117,7 +117,7 @@ __global__ void quant_v_pack_kernel(const uint16_t* __restrict__ src, int L_cap,
     vcode_inverse(D, BITS, byte, k, tau, c);
     const int t = blk * 32 + tau;
     const float x = bf16_to_f32(src[((size_t)unit * L_cap + t) * D + c]);
-    const H2 m = meta[((size_t)unit * n_quant + t) * (D / 32) + c / 32];
+    const H2 m = meta[(((size_t)unit * (n_quant / 32) + t / 32) * (D / 32) + c / 32) * 32 + vmeta_slot(tau)];
     v |= code_of(x, (float)m.s, (float)m.z, QMAX) << (BITS * k);
   }
   codes[(size_t)unit * n_quant * D * BITS / 8 + gid] = (uint8_t)v;
@@ -141,8 +141,18 @@ __global__ void dequant_kernel(const uint8_t* __restrict__ codes, const H2* __re
     vcode_locate(D, bits, t % 32, d, byte, shift);
     c = (codes[(size_t)(t / 32) * 4 * D * bits + byte] >> shift) & ((1u << bits) - 1u);
   }
-  const H2 m = which == 0 ? meta[(size_t)(t / 32) * D + d] : meta[(size_t)t * (D / 32) + d / 32];
-  out[idx] = fmaf((float)c, (float)m.s, (float)m.z);
+  float s, z;
+  if (which == 0) {
+    const _Float16* plane = reinterpret_cast<const _Float16*>(meta + (size_t)(t / 32) * D);
+    const int pos = kmeta_pos(D, bits, d);
+    s = (float)plane[pos];
+    z = (float)plane[D + pos];
+  } else {
+    const H2 m = meta[((size_t)(t / 32) * (D / 32) + d / 32) * 32 + vmeta_slot(t % 32)];
+    s = (float)m.s;
+    z = (float)m.z;
+  }
+  out[idx] = fmaf((float)c, s, z);
 }
 
 }  // namespace
@@ -204,7 +214,7 @@ extern "C" int vc_debug_dequant(const vc_kv_comp* comp, int B, int Hkv, int D, i
   const int row_bytes = D * comp->bits / 8;
   const uint8_t* codes = (which == 0 ? comp->k_codes : comp->v_codes) + unit * nq * row_bytes;
   const H2* meta = reinterpret_cast<const H2*>(which == 0 ? comp->k_meta : comp->v_meta);
-  meta += which == 0 ? unit * (nq / 32) * D : unit * nq * (D / 32);
+  meta += unit * (nq / 32) * D;  // both: D dwords per 32-token block
   VC_CHECK(codes && meta, "vc_debug_dequant: null codes/meta");
   const int n = nq * D;
   dequant_kernel<<<(n + 255) / 256, 256, 0, stream>>>(codes, meta, comp->bits, nq, D, which, out);

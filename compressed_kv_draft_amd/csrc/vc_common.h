@@ -83,6 +83,24 @@ __host__ __device__ inline void vcode_inverse(int D, int bits, int byte, int k, 
   c = 16 * ct + lane % 16;
 }
 
+// K metadata of one 32-token block: a plane of D f16 scales, then a plane of D
+// f16 zeros, both in "pair order": channel c sits at f16 index kmeta_pos(c), so
+// that dword w of a plane holds the two channels whose codes one code dword
+// carries at bits b and b + 16 (the matrix-core operand pairs).
+__host__ __device__ inline int kmeta_pos(int D, int bits, int c) {
+  const int cpd = 32 / bits, ppd = cpd / 2, nks = D / 32;
+  const int quad = c / (D / 4), r = c % (D / 4);
+  const int d = r / cpd, rem = r % cpd;
+  const int h = rem / ppd, j = rem % ppd;
+  const int pi = d * ppd + j;
+  return 2 * ((quad * nks + pi / 4) * 4 + pi % 4) + h;
+}
+
+// V metadata of one 32-token block: [D/32 groups][32 slots] {scale, zero}; token
+// tau of the block sits in slot 8 ((tau % 16) / 4) + tau % 4 + 4 (tau / 16), the
+// token order of the score tiles.
+__host__ __device__ inline int vmeta_slot(int tau) { return 8 * ((tau % 16) / 4) + tau % 4 + 4 * (tau / 16); }
+
 struct Partial {  // split-K partial of one (row): unnormalised o, running max (log2 units), sum
   float m, l;
 };

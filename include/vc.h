@@ -64,10 +64,19 @@ extern "C" {
  *              bit = bits * j + 16 * hf,
  *              byte = lane * (D*bits/16) + 4 * dword + bit / 8,
  *            code at bit (bit % 8) of that byte.  vc_quantize_kv writes it.
- *   k_meta   f16x2 [B][Hkv][n_quant/32][D]   {scale, zero} of the group formed
- *            by 32 consecutive tokens of one channel.
- *   v_meta   f16x2 [B][Hkv][n_quant][D/32]   {scale, zero} of the group formed
- *            by 32 consecutive channels of one token.
+ *   k_meta   f16 [B][Hkv][n_quant/32][2][D]  per 32-token block, a plane of
+ *            the scales and then a plane of the zeros of the groups formed by
+ *            the block's 32 tokens of one channel, each plane in pair order:
+ *            channel c (quad = c / (D/4), r = c % (D/4), cpd = 32/bits,
+ *            ppd = cpd/2, d = r / cpd, h = (r % cpd) / ppd, j = r % ppd,
+ *            pi = d * ppd + j) sits at
+ *              2 * ((quad * (D/32) + pi / 4) * 4 + pi % 4) + h,
+ *            so that each dword pairs the two channels one K code dword holds
+ *            at bits b and b + 16.
+ *   v_meta   f16x2 [B][Hkv][n_quant/32][D/32][32]  {scale, zero} of the group
+ *            formed by 32 consecutive channels of one token; token tau of a
+ *            block sits in slot 8 * ((tau % 16) / 4) + tau % 4 + 4 * (tau / 16).
+ *   All four arrays must be 16-byte aligned for vc_draft_attn.
  *   Dequantised value = fp32(code * scale + zero), a single rounding.
  *   Inputs must keep |q| * K scale < 4096 and |V| scale * 256 < 65504 (the
  *   draft kernel carries these products in f16).

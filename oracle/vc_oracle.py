@@ -156,6 +156,44 @@ def pack_v_codes_tiled(codes: np.ndarray, bits: int) -> np.ndarray:
     return out.reshape(-1).astype(np.uint8)
 
 
+def pack_k_meta(s: np.ndarray, z: np.ndarray, bits: int) -> np.ndarray:
+    """K scales and zeros [n/32, D] (fp16) into the C header's k_meta layout
+    (include/vc.h, QUANT layout): per block a scale plane then a zero plane,
+    channel c of each at f16 index
+      quad = c // (D/4), r = c % (D/4), cpd = 32 // bits, ppd = cpd // 2,
+      d = r // cpd, h = (r % cpd) // ppd, j = r % ppd, pi = d ppd + j,
+      pos = 2 ((quad (D/32) + pi // 4) 4 + pi % 4) + h.
+    Returns the raw fp16 bit patterns, uint16 [n/32, 2, D]."""
+    nb, D = s.shape
+    cpd = 32 // bits
+    ppd = cpd // 2
+    out = np.zeros((nb, 2, D), dtype=np.uint16)
+    for c in range(D):
+        quad, r = divmod(c, D // 4)
+        d, rem = divmod(r, cpd)
+        h, j = divmod(rem, ppd)
+        pi = d * ppd + j
+        pos = 2 * ((quad * (D // 32) + pi // 4) * 4 + pi % 4) + h
+        out[:, 0, pos] = s[:, c].view(np.uint16)
+        out[:, 1, pos] = z[:, c].view(np.uint16)
+    return out
+
+
+def pack_v_meta(s: np.ndarray, z: np.ndarray) -> np.ndarray:
+    """V scales and zeros [n, D/32] (fp16) into the header's v_meta layout:
+    [n/32][D/32 groups][32 slots]{scale, zero}, token tau of a block in slot
+    8 ((tau % 16) // 4) + tau % 4 + 4 (tau // 16).  uint16 [n/32, D/32, 32, 2]."""
+    n, G = s.shape
+    assert n % GROUP == 0
+    nb = n // GROUP
+    out = np.zeros((nb, G, 32, 2), dtype=np.uint16)
+    for tau in range(32):
+        slot = 8 * ((tau % 16) // 4) + tau % 4 + 4 * (tau // 16)
+        out[:, :, slot, 0] = s[tau::32].view(np.uint16)
+        out[:, :, slot, 1] = z[tau::32].view(np.uint16)
+    return out
+
+
 # ----------------------------------------------------------------------------
 # attention  [VC Core Algorithm: drafting with KV_comp, verification with KV_full]
 # ----------------------------------------------------------------------------

@@ -162,6 +162,44 @@ def test_pack_v_tiled_positions_and_bijection():
         assert pop(O.pack_v_codes_tiled(one, b_)) == b_
 
 
+def test_pack_meta_positions_and_pairing():
+    """K/V metadata layouts (include/vc.h): hand-derived positions, and the
+    property the K layout exists for -- each dword of a plane pairs the two
+    channels that one packed K code dword carries at bits b and b + 16."""
+    def kpos(D, bits, c):
+        s = np.zeros((1, D), np.float16)
+        s[0, c] = 1.0
+        out = O.pack_k_meta(s, np.zeros_like(s), bits)
+        nz = np.nonzero(out[0, 0])[0]
+        assert len(nz) == 1 and not out[0, 1].any()
+        return int(nz[0])
+    # int2, D 128: channel 0 -> 0; 8 -> h 1 -> 1; 1 -> pi 1 -> 2; 16 -> d 1, pi 8 -> ks 2 -> 16; 32 -> quad 1 -> 32
+    assert [kpos(128, 2, c) for c in (0, 8, 1, 16, 32)] == [0, 1, 2, 16, 32]
+    # int4, D 128: channel 4 -> h 1 -> 1; 9 -> d 1, j 1 -> pi 5 -> ks 1, i 1 -> 2 (4 + 1) = 10
+    assert [kpos(128, 4, c) for c in (4, 9)] == [1, 10]
+    for D, bits in [(64, 2), (64, 4), (128, 2), (128, 4)]:
+        per = 8 // bits
+        pos = [kpos(D, bits, c) for c in range(D)]
+        assert sorted(pos) == list(range(D))
+        for c1 in range(D):
+            c2 = pos.index(pos[c1] ^ 1)
+            if pos[c1] % 2:
+                continue
+            # bit of channel c in a packed code row (pack_codes): byte c // per, bit bits (c % per)
+            b1 = 8 * (c1 // per) + bits * (c1 % per)
+            b2 = 8 * (c2 // per) + bits * (c2 % per)
+            assert b1 // 32 == b2 // 32 and b2 % 32 == b1 % 32 + 16, (D, bits, c1, c2)
+    # V: token tau -> slot 8 ((tau % 16) // 4) + tau % 4 + 4 (tau // 16); groups keep their order
+    n, G = 64, 4
+    s = np.arange(n * G, dtype=np.float16).reshape(n, G)
+    out = O.pack_v_meta(s, -s)
+    assert out[0, 0, 0, 0] == s[0, 0].view(np.uint16)
+    assert out[0, 0, 4, 0] == s[16, 0].view(np.uint16)        # tau 16 -> slot 4
+    assert out[0, 2, 8 + 1, 0] == s[5, 2].view(np.uint16)     # tau 5 -> slot 9
+    assert out[1, 3, 8 * 3 + 4 + 3, 1] == (-s[32 + 31, 3]).view(np.uint16)  # tau 31 -> slot 31
+    assert sorted(out[..., 0].reshape(-1).tolist()) == sorted(s.view(np.uint16).reshape(-1).tolist())
+
+
 def test_dequant_fraction_exact():
     rng = np.random.default_rng(2)
     codes = rng.integers(0, 16, (64, 64)).astype(np.uint8)

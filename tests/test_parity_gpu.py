@@ -103,14 +103,12 @@ def test_quantize_bit_exact(D, bits):
             vf = O.bf16_to_f64(V[b, h, :nq]).astype(np.float32)
             c, s, z = O.quantize_k(kf, bits)
             assert np.array_equal(kc[b, h], O.pack_codes(c, bits)), (b, h, "k codes")
-            assert np.array_equal(km[b, h, ..., 0].view(np.uint16), s.view(np.uint16)), (b, h, "k scale")
-            assert np.array_equal(km[b, h, ..., 1].view(np.uint16), z.view(np.uint16)), (b, h, "k zero")
+            assert np.array_equal(km[b, h].view(np.uint16), O.pack_k_meta(s, z, bits)), (b, h, "k meta")
             dq = vc.debug_dequant(comp, w.B, w.Hkv, D, b, h, 0).cpu().numpy()
             assert np.array_equal(dq.astype(np.float64), O.dequant_k(c, s, z)), (b, h, "k dequant")
             c, s, z = O.quantize_v(vf, bits)
             assert np.array_equal(vcd[b, h].reshape(-1), O.pack_v_codes_tiled(c, bits)), (b, h, "v codes")
-            assert np.array_equal(vm[b, h, ..., 0].view(np.uint16), s.view(np.uint16)), (b, h, "v scale")
-            assert np.array_equal(vm[b, h, ..., 1].view(np.uint16), z.view(np.uint16)), (b, h, "v zero")
+            assert np.array_equal(vm[b, h].view(np.uint16), O.pack_v_meta(s, z)), (b, h, "v meta")
             dq = vc.debug_dequant(comp, w.B, w.Hkv, D, b, h, 1).cpu().numpy()
             assert np.array_equal(dq.astype(np.float64), O.dequant_v(c, s, z)), (b, h, "v dequant")
 
