@@ -687,48 +687,46 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
 }
 
 // Merge the split partials (o unnormalised, m in log2 units, l) of one (b, h)
-// row per workgroup: the splits' maxima and sums go through LDS, then every
-// thread reads its channel of all splits with independent loads.
+// row per workgroup, one thread per channel.  The channel values of the first
+// kCombineChunk splits are loaded while the splits' maxima and sums go to LDS,
+// so that up to kCombineChunk splits cost one memory latency and one barrier.
+constexpr int kCombineChunk = 16;
 constexpr int kMaxCombineSplits = 256;
 __global__ __launch_bounds__(128) void draft_combine_kernel(const float* __restrict__ ws, int splits, int rows,
                                                             int D, float* __restrict__ out,
                                                             float* __restrict__ lse) {
-  __shared__ float s_f[kMaxCombineSplits], s_l[kMaxCombineSplits];
-  __shared__ float s_M, s_L;
-  const int row = blockIdx.x;
-  for (int s = threadIdx.x; s < splits; s += blockDim.x) {
-    const float* p = ws + ((size_t)s * rows + row) * (D + 2);
-    s_f[s] = p[D];
-    s_l[s] = p[D + 1];
+  __shared__ float s_m[kMaxCombineSplits], s_l[kMaxCombineSplits];
+  const int row = blockIdx.x, d = threadIdx.x;
+  float o[kCombineChunk];
+#pragma unroll
+  for (int j = 0; j < kCombineChunk; ++j)
+    o[j] = j < splits ? ws[((size_t)j * rows + row) * (D + 2) + d] : 0.0f;
+  for (int sp = d; sp < splits; sp += blockDim.x) {
+    const float* p = ws + ((size_t)sp * rows + row) * (D + 2);
+    s_m[sp] = p[D];
+    s_l[sp] = p[D + 1];
   }
   __syncthreads();
-  if (threadIdx.x < 64) {
-    float M = kNegInf;
-    for (int s = threadIdx.x; s < splits; s += 64) M = fmaxf(M, s_f[s]);
+  float M = kNegInf;
+  for (int sp = 0; sp < splits; ++sp) M = fmaxf(M, s_m[sp]);
+  float L = 0.0f, O = 0.0f;
+  if (M != kNegInf) {
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
-    float L = 0.0f;
-    for (int s = threadIdx.x; s < splits; s += 64) {
-      const float f = s_f[s] == kNegInf ? 0.0f : fast_exp2(s_f[s] - M);
-      s_f[s] = f;
-      L += s_l[s] * f;
+    for (int j = 0; j < kCombineChunk; ++j) {
+      if (j < splits) {
+        const float w = s_m[j] == kNegInf ? 0.0f : fast_exp2(s_m[j] - M);
+        L = fmaf(s_l[j], w, L);
+        O = fmaf(o[j], w, O);
+      }
     }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) L += __shfl_xor(L, m, 64);
-    if (threadIdx.x == 0) {
-      s_M = M;
-      s_L = L;
+    for (int sp = kCombineChunk; sp < splits; ++sp) {
+      const float w = s_m[sp] == kNegInf ? 0.0f : fast_exp2(s_m[sp] - M);
+      L = fmaf(s_l[sp], w, L);
+      O = fmaf(ws[((size_t)sp * rows + row) * (D + 2) + d], w, O);
     }
   }
-  __syncthreads();
-  const float L = s_L;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float O = 0.0f;
-#pragma unroll 8
-    for (int s = 0; s < splits; ++s) O += ws[((size_t)s * rows + row) * (D + 2) + d] * s_f[s];
-    out[(size_t)row * D + d] = L > 0.0f ? O / L : 0.0f;
-  }
-  if (lse != nullptr && threadIdx.x == 0) lse[row] = L > 0.0f ? (s_M + __log2f(L)) * kLn2 : kNegInf;
+  out[(size_t)row * D + d] = L > 0.0f ? O / L : 0.0f;
+  if (lse != nullptr && d == 0) lse[row] = L > 0.0f ? (M + __log2f(L)) * kLn2 : kNegInf;
 }
 
 // Workspace: the split partials.
@@ -888,12 +886,12 @@ extern "C" int vc_draft_attn(const vc_kv_comp* comp, const vc_tail* tail, const 
   const DraftKernel kern = D == 128 ? (nv == 2 ? pick_kernel<128, 2>(bits) : pick_kernel<128, 1>(bits))
                                     : pick_kernel<64, 1>(bits);
   const DraftPlan p = plan_draft(units, main_blocks, tail_blocks, wgs_per_cu(kern));
+  VC_CHECK(p.splits <= kMaxCombineSplits, "vc_draft_attn: %d splits exceed %d", p.splits, kMaxCombineSplits);
   const size_t need = draft_ws_need(B, Hq, Hkv, D, p.splits);
   if (p.splits > 1) {
     if (ws == nullptr || ws_bytes < need)
       return fail(VC_ERR_WORKSPACE, "vc_draft_attn: workspace %zu < %zu bytes", ws_bytes, need);
     VC_CHECK(aligned(ws, 16), "vc_draft_attn: workspace misaligned");
-    VC_CHECK(p.splits <= kMaxCombineSplits, "vc_draft_attn: %d splits exceed %d", p.splits, kMaxCombineSplits);
     a.ws = static_cast<float*>(ws);
   }
   a.main_splits = p.main_splits;
@@ -904,7 +902,7 @@ extern "C" int vc_draft_attn(const vc_kv_comp* comp, const vc_tail* tail, const 
   kern<<<grid, kThreads, 0, stream>>>(a);
   VC_HIP(hipGetLastError());
   if (p.splits > 1) {
-    draft_combine_kernel<<<B * Hq, 128, 0, stream>>>(a.ws, p.splits, B * Hq, D, out, lse);
+    draft_combine_kernel<<<B * Hq, D, 0, stream>>>(a.ws, p.splits, B * Hq, D, out, lse);
     VC_HIP(hipGetLastError());
   }
   return VC_OK;
