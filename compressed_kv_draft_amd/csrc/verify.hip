@@ -383,8 +383,11 @@ Plan plan_verify(int B, int Hq, int Hkv, int n_q, int max_ctx, int wpc) {
   const int g = Hq / Hkv;
   const int R = g * n_q;
   const int NT = (R + 15) / 16;
-  p.rowgroups = (NT + kWaves * kMaxMT - 1) / (kWaves * kMaxMT);
-  const int per_group = (NT + p.rowgroups - 1) / p.rowgroups;
+  // full row groups of kWaves * kMaxMT tiles (every wavefront equally loaded)
+  // and one remainder group: a workgroup holds its slot for as long as its
+  // busiest wavefront runs, so this beats spreading the tiles evenly
+  const int per_group = NT < kWaves * kMaxMT ? NT : kWaves * kMaxMT;
+  p.rowgroups = (NT + per_group - 1) / per_group;
   p.mt = (per_group + kWaves - 1) / kWaves;
   p.tiles_per_group = per_group;
   const int units = B * Hkv * p.rowgroups;
