@@ -31,6 +31,9 @@ def parse():
     p.add_argument("--config", default="llama3_8b_layer_b8_l32k_int2_k32")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-units", type=int, default=8, help="(b, kv-head) units in the CPU oracle sample")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="run only a plain 1 GiB device-to-device copy, 3 times (the reference kernel for "
+                        "scaling the FETCH_SIZE / WRITE_SIZE counters to bytes)")
     p.add_argument("--stagger", action="store_true",
                    help="measure the full-KV prefetch of one request group against the other group's drafting "
                         "(Llama-70B-shaped paged workload) and print that JSON line instead")
@@ -155,6 +158,49 @@ def stagger(a):
     print(json.dumps(line), flush=True)
 
 
+def calibrate_copy():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n, "launches": 3}),
+          flush=True)
+
+
+def kernel_source_digest():
+    """sha256 of the draft kernel's sources: ties a stored counter reading to the code it was taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("draft.hip", "mfma.h", "vc_common.h"):
+        with open(os.path.join(ROOT, "compressed_kv_draft_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per vc_draft_attn call from the committed counter summary of this
+    workload (profiles/hbm_traffic_draft_<workload>.txt), or None when there is
+    none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_draft_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(w, dw, n_accept_sum, units):
     """Time the fp64 oracle on a bounded sample of the same workload: for `units`
     (b, kv-head) slices, every draft step of the round and the verify pass (the
@@ -196,6 +242,9 @@ def main():
         sys.exit(2)
     if a.stagger:
         stagger(a)
+        return
+    if a.calibrate_copy:
+        calibrate_copy()
         return
     import numpy as np
     import torch
@@ -272,7 +321,8 @@ def main():
     roof = {"bound": "hbm", "kernel": "vc_draft_attn (draft_mfma_kernel + draft_combine_kernel)"
             if dominant == "draft" else "vc_verify_attn (verify_mfma_kernel + verify_combine_kernel)",
             "achieved": round(d_gbs if dominant == "draft" else v_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round((d_gbs if dominant == "draft" else v_gbs) / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round((d_gbs if dominant == "draft" else v_gbs) / HBM_PEAK_GBS, 4),
+            "traffic": stored_traffic(w.name) if dominant == "draft" else None,
             "bytes_per_launch": int(d_bytes if dominant == "draft" else v_bytes),
             "avg_launch_us": round(1e6 * (d_avg if dominant == "draft" else v_avg), 2)}
     step_s = wall / a.steps
