@@ -7,10 +7,9 @@
 // P.V are thin matrix products (g rows).  With int2/int4 codes they carry 20-26
 // multiply-adds per HBM byte, more than fp32 vector ALUs sustain at HBM speed,
 // so both products run on the f16 matrix cores, exactly:
-//  * a code c placed in the mantissa of an f16 bit pattern is the subnormal
-//    c * 2^(bits*jj - 24) (jj = its position in the byte) -- a shift and an AND
-//    turn two packed codes into two exact f16 operands (always at one of the
-//    byte's two highest positions, see code_target);
+//  * a code c placed at bit p of the mantissa of an f16 bit pattern is the
+//    subnormal c * 2^(p - 24) -- a shift and an AND turn two packed codes into
+//    two exact f16 operands (always at p >= 4, see code_target);
 //  * K is grouped per channel, so its scale goes into the query: q_h * s is
 //    computed in f16 as hi + lo (a rounded product and its exact residual, one
 //    fma), giving 22 significand bits; hi and lo are adjacent MFMA columns;
@@ -128,6 +127,8 @@ struct Cfg {
   static constexpr int B_ = BITS > 0 ? BITS : 2;
   static constexpr int CPD = 32 / B_;  // K channels per code dword
   static constexpr int PPD = CPD / 2;  // code pairs per dword
+  // V channel tile ct always takes pair ct % PPD when the tiles cover a whole dword
+  static constexpr bool VWIDE = NCT >= PPD;
   static constexpr int PER = 8 / B_;   // codes per byte
   static constexpr uint32_t MASK = B_ == 2 ? 0x00030003u : 0x000F000Fu;
   static constexpr int KDW = D * B_ / 128;  // K code dwords per lane per 16-token tile
@@ -162,23 +163,33 @@ struct Cfg {
   static constexpr int WAVES = cmin(4, kLdsPerCu / SMEM);
 };
 
-// Position inside its byte at which code pair j of a dword is handed to the
-// matrix cores: always one of the two highest (int2: 2 or 3, int4: 1).  The f16
-// products sum with a truncating internal alignment when their magnitudes
-// differ widely; keeping the code operands at least 2^(4-24) avoids the large
-// systematic bias the lowest subnormals (2^-24) showed on the device.
-template <int BITS>
+// Bit position (in units of `bits`, inside its 16-bit half) at which code pair j
+// of a dword is handed to the matrix cores.  The f16 products sum with a
+// truncating internal alignment when their magnitudes differ widely; keeping
+// every code operand at least 2^(4-24) avoids the systematic bias the lowest
+// subnormals (2^-24) showed on the device.  int4: bits 4..7 (jt 1).  int2,
+// WIDE: bits 4..9 (jt 2, 3, 4), reached with two shift amounts per dword (<< 4
+// for pairs 0-1, none for 2-4, >> 6 for 5-7); otherwise bits 4..7 by parity of
+// j (three shift amounts), for operands whose channel takes pairs j and j + 4.
+template <int BITS, bool WIDE>
 __host__ __device__ constexpr int code_target(int j) {
-  return BITS == 4 ? 1 : 2 + ((j % (8 / BITS)) & 1);
+  if constexpr (BITS == 4) {
+    return 1;
+  } else if constexpr (WIDE) {
+    constexpr int t[8] = {2, 3, 2, 3, 4, 2, 3, 4};
+    return t[j % 8];
+  } else {
+    return 2 + ((j % 4) & 1);
+  }
 }
 
 // Two packed codes (bits b and b+16 of w, pair position j of the dword) as an
 // f16 pair: code * 2^(bits * code_target(j) - 24) each, exactly.
-template <int BITS>
+template <int BITS, bool WIDE>
 __device__ __forceinline__ uint32_t code_pair(uint32_t w, int j) {
   constexpr int PER = 8 / BITS;
   constexpr uint32_t MASK = BITS == 2 ? 0x00030003u : 0x000F000Fu;
-  const int jt = code_target<BITS>(j);
+  const int jt = code_target<BITS, WIDE>(j);
   const int sh = 8 * (j / PER) + BITS * (j % PER) - BITS * jt;
   const uint32_t ws = sh >= 0 ? (w >> sh) : (w << -sh);
   return ws & (MASK << (BITS * jt));
@@ -418,7 +429,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
             const int pi = 4 * ks + i, d = pi / C::PPD, j = pi % C::PPD;
             const int ca = C::CPD * d + j, cb = ca + C::CPD / 2;
             const float xa = bf16_to_f32(qh[ca]), xb = bf16_to_f32(qh[cb]);
-            const float f = __builtin_ldexpf(1.0f, kQExp - BITS * code_target<BITS>(j));
+            const float f = __builtin_ldexpf(1.0f, kQExp - BITS * code_target<BITS, true>(j));
             const f16x2 pf = {(_Float16)(xa * f), (_Float16)(xb * f)};
             const f16x2 pz = {(_Float16)xa, (_Float16)xb};
             qF[ks][i] = __builtin_bit_cast(uint32_t, pf);
@@ -522,7 +533,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int pi = 4 * ks + i;
-              a4[i] = code_pair<BITS>(kw[pi / C::PPD], pi % C::PPD);
+              a4[i] = code_pair<BITS, true>(kw[pi / C::PPD], pi % C::PPD);
             }
             acc = mfma_f16(__builtin_bit_cast(f16x8, a4), qt[ks], acc);
           }
@@ -569,7 +580,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int pi = i * NCT + ct;
-            b4[i] = code_pair<BITS>(vw[pi / C::PPD], pi % C::PPD);
+            b4[i] = code_pair<BITS, C::VWIDE>(vw[pi / C::PPD], pi % C::PPD);
           }
           st.O[ct] = mfma_f16(Ahi[v], __builtin_bit_cast(f16x8, b4), st.O[ct]);
           st.O[ct] = mfma_f16(Alo[v], __builtin_bit_cast(f16x8, b4), st.O[ct]);
@@ -641,7 +652,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
   for (int ct = 0; ct < NCT; ++ct) {
     if (quant_wg) {
       constexpr int B2 = BITS > 0 ? BITS : 2;
-      const float osc = __builtin_ldexpf(1.0f, 24 - B2 * code_target<B2>(ct % Cfg<D, B2>::PPD));
+      const float osc = __builtin_ldexpf(1.0f, 24 - B2 * code_target<B2, Cfg<D, B2>::VWIDE>(ct % Cfg<D, B2>::PPD));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * quad + i;
