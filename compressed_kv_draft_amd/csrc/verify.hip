@@ -85,7 +85,9 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
   if (su >= a.n_su) return;
   const int split = su % a.splits, unit = su / a.splits;
   const int b = unit / a.Hkv, hk = unit % a.Hkv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // wave-uniform (scalar) so that the tile guards below are scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, quad = lane >> 4;
 
   int ctx = a.ctx_len[b];
@@ -122,6 +124,10 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
     l[i] = 0.0f;
   }
   const bool wave_live = tile0 + wave < tile_end;
+  // Only the last query tile needs a liveness guard: a wavefront with any live
+  // tile computes its earlier tiles unconditionally.  A dead one has zero
+  // queries and rlim = -1 and is never written out.
+  const bool last_live = tile0 + wave + kWaves * (MT - 1) < tile_end;
 
   // register staging, two tiles deep: chunk c -> key c / (D/8), 8 channels at (c % (D/8)) * 8
   int ck[CPT], cc[CPT];
@@ -198,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
               *reinterpret_cast<const bf16x8*>(&Ks[buf][(16 * h + col) * KP + quad * (D / 4) + 8 * ks]);
 #pragma unroll
           for (int i = 0; i < MT; ++i)
-            if (tile0 + wave + kWaves * i < tile_end) s[i][h] = mfma_bf16(ka, qb[i][ks], s[i][h]);
+            if (i < MT - 1 || last_live) s[i][h] = mfma_bf16(ka, qb[i][ks], s[i][h]);
         }
       }
       // mask only tiles that reach the drafted rows or the end of the range
@@ -206,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
       f16x8 A[MT];
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
-        if (tile0 + wave + kWaves * i >= tile_end) {
+        if (i == MT - 1 && !last_live) {
           A[i] = f16x8{};
           continue;
         }
@@ -264,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
         const f16x8 bv = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int i = 0; i < MT; ++i)
-          if (tile0 + wave + kWaves * i < tile_end) O[i][ct] = mfma_f16(A[i], bv, O[i][ct]);
+          if (i < MT - 1 || last_live) O[i][ct] = mfma_f16(A[i], bv, O[i][ct]);
       }
     }
     __syncthreads();
