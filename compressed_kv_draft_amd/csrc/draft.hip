@@ -29,6 +29,7 @@
 #include <map>
 #include <mutex>
 
+#include "lds_dma.h"
 #include "mfma.h"
 #include "vc_common.h"
 
@@ -70,54 +71,6 @@ constexpr int kQExp = 4;      // q is scaled by 2^kQExp before it multiplies the
 constexpr int cmax(int x, int y) { return x > y ? x : y; }
 constexpr int cmin(int x, int y) { return x < y ? x : y; }
 constexpr int kLdsPerCu = 160 * 1024;
-
-// Direct global -> LDS copies: each load instruction moves 16 bytes per lane,
-// lane i's to LDS byte 16 i of its 1 KiB (gfx950 global_load_lds_dwordx4, LDS
-// base address in M0).  Issued from inline assembly so that the compiler does
-// not see them: it would otherwise wait for every outstanding one (vmcnt(0))
-// before any LDS read it cannot prove disjoint, which defeats the prefetch.
-// M0 is saved and restored around the load.
-constexpr int lds_dma_count(int bytes) { return (bytes + 1023) / 1024; }
-
-__device__ __forceinline__ void lds_dma16(const unsigned char* base, uint32_t voff, uint32_t lds_addr) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(base), "s"(lds_addr)
-      : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-  using lptr = __attribute__((address_space(3))) const void*;
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lptr)p);
-}
-
-// BYTES from the wave-uniform address gbase to the wave-uniform LDS address lds;
-// voff = 16 * lane.
-template <int BYTES>
-__device__ __forceinline__ void lds_dma(const unsigned char* gbase, uint32_t voff, uint32_t lds, int lane) {
-  static_assert(BYTES % 16 == 0, "");
-#pragma unroll
-  for (int k = 0; k < BYTES / 1024; ++k) lds_dma16(gbase + 1024 * k, voff, lds + 1024 * k);
-  if constexpr (BYTES % 1024 != 0) {
-    constexpr int k = BYTES / 1024;
-    if (lane < (BYTES % 1024) / 16) lds_dma16(gbase + 1024 * k, voff, lds + 1024 * k);
-  }
-}
-
-// Waits for those loads are explicit.  Loads complete in order, so "at most N outstanding" means all but the last N
-// load instructions have written LDS.
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <int D, int BITS>
 struct Cfg {

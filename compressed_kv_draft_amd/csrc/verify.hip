@@ -23,6 +23,7 @@
 #include <mutex>
 #include <type_traits>
 
+#include "lds_dma.h"
 #include "mfma.h"
 #include "vc_common.h"
 
@@ -33,6 +34,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kKT = 32;       // keys per tile
 constexpr int kMaxMT = 3;     // query tiles per wavefront
+constexpr int kDepth = 4;     // K/V tiles in the LDS ring
 constexpr float kTau = 8.0f;  // lazy rescale threshold (log2 units)
 
 struct VerifyArgs {
@@ -69,12 +71,13 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 w) {
 template <int D, int MT, bool PAGED>
 __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
   constexpr int NKS = D / 32, NCT = D / 16;
-  constexpr int KP = D + 8;                          // K row pitch (elements)
-  constexpr int VP = D + 16;                         // V row pitch (elements)
-  constexpr int CH = kKT * D / 8;                    // 16-byte chunks per tile (K or V)
-  constexpr int CPT = (CH + kThreads - 1) / kThreads;  // chunks per thread
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKT * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kKT * VP];
+  constexpr int CPR = D / 8;                      // 16-byte chunks per key row
+  constexpr int TILE = kKT * D * 2;               // bytes of one K or V tile
+  constexpr int ROUNDS = TILE / (16 * kThreads);  // direct loads per thread per tile and tensor
+  static_assert(TILE % (16 * kThreads) == 0, "a tile is whole rounds of 16-byte loads");
+  constexpr int NDMA = 2 * ROUNDS;                // load instructions per thread per tile
+  // ring of kDepth K tiles, then kDepth V tiles (bf16 as loaded, f16 once converted)
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kDepth * TILE];
 
   // workgroup -> (row group, split, unit): the row groups of one (split, unit)
   // are 8 workgroups apart, i.e. on the same XCD under round-robin dispatch
@@ -129,68 +132,111 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
   // queries and rlim = -1 and is never written out.
   const bool last_live = tile0 + wave + kWaves * (MT - 1) < tile_end;
 
-  // register staging, two tiles deep: chunk c -> key c / (D/8), 8 channels at (c % (D/8)) * 8
-  int ck[CPT], cc[CPT];
-#pragma unroll
-  for (int u = 0; u < CPT; ++u) {
-    const int c = threadIdx.x + u * kThreads;
-    ck[u] = c < CH ? c / (D / 8) : kKT;  // kKT: never a valid key offset
-    cc[u] = (c % (D / 8)) * 8;
-  }
+  // Staging: tile t's K and V go to ring slot t % kDepth by direct 16-byte
+  // global->LDS loads issued kDepth - 1 tiles ahead; no registers hold them in flight.
+  // In round r this thread fills LDS chunk s = (r * kWaves + wave) * 64 + lane
+  // of the tile, which holds 16-byte chunk (s % CPR) ^ (key % CPR) of key row
+  // key = s / CPR: the XOR swizzle makes the operand reads below conflict-free.
+  // The rows of one load instruction lie in one page (pages hold >= 8 rows).
+  const uint32_t lds0 = lds_address(smem);
+  const unsigned char* kv8 = reinterpret_cast<const unsigned char*>(a.k);
+  const unsigned char* vv8 = reinterpret_cast<const unsigned char*>(a.v);
   const size_t unit_row0 = (size_t)(b * a.Hkv + hk) * a.L_cap;
-  const int pt_mask = (1 << a.page_log2) - 1;
-  const size_t page_elems = (size_t)a.Hkv * 2 * (pt_mask + 1) * D;
-  u32x4 kreg[2][CPT], vreg[2][CPT];
-  auto load_tile = [&](int t0, int set) {
+  const int page_rows = 1 << a.page_log2;
+  const size_t page_bytes = (size_t)a.Hkv * 2 * page_rows * D * 2;
+  using cptr = const __attribute__((address_space(4))) int32_t*;  // scalar reads: uniform indices
+  const cptr ptab = (cptr)(a.page_table);
+  uint32_t zfill = 0;  // bit (slot * ROUNDS + r): that round of that ring slot reads as zeros
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const int t0 = kb + t * kKT;
+    const int sl = t % kDepth;
+    const uint32_t kl = lds0 + sl * TILE, vl = lds0 + (kDepth + sl) * TILE;
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int key = t0 + ck[u];
-      kreg[set][u] = u32x4{0u, 0u, 0u, 0u};
-      vreg[set][u] = u32x4{0u, 0u, 0u, 0u};
-      if (ck[u] < kKT && key < ke) {
-        if constexpr (PAGED) {
-          const int slot = a.page_table[(size_t)b * a.pages_per_seq + (key >> a.page_log2)];
-          if (slot >= 0 && slot < a.n_slots) {
-            const uint16_t* kp =
-                a.k + (size_t)slot * page_elems + ((size_t)(hk * 2) * (pt_mask + 1) + (key & pt_mask)) * D + cc[u];
-            kreg[set][u] = *reinterpret_cast<const u32x4*>(kp);
-            vreg[set][u] = *reinterpret_cast<const u32x4*>(kp + (size_t)(pt_mask + 1) * D);
-          }
-        } else {
-          const size_t off = (unit_row0 + key) * D + cc[u];
-          kreg[set][u] = *reinterpret_cast<const u32x4*>(a.k + off);
-          vreg[set][u] = *reinterpret_cast<const u32x4*>(a.v + off);
-        }
+    for (int r = 0; r < ROUNDS; ++r) {
+      const int s = (r * kWaves + wave) * 64 + lane;
+      const int row = s / CPR, cc = (s % CPR) ^ (row % CPR);
+      // rows past the split's range are clamped to its last row (masked later)
+      const int key = min(t0 + row, ke - 1);
+      const unsigned char *kp, *vp;
+      if constexpr (PAGED) {
+        const int key0 = min(t0 + (r * kWaves + wave) * (64 / CPR), ke - 1);  // wave-uniform
+        int pslot = ptab[(size_t)b * a.pages_per_seq + (key0 >> a.page_log2)];
+        const bool bad = pslot < 0 || pslot >= a.n_slots;
+        const uint32_t bit = 1u << (sl * ROUNDS + r);
+        zfill = bad ? (zfill | bit) : (zfill & ~bit);
+        if (bad) pslot = 0;  // a readable page; the chunk is zero-filled before use
+        kp = kv8 + (size_t)pslot * page_bytes +
+             ((size_t)(hk * 2) * page_rows + (key & (page_rows - 1))) * D * 2 + cc * 16;
+        vp = kp + (size_t)page_rows * D * 2;
+      } else {
+        kp = kv8 + ((unit_row0 + key) * D) * 2 + cc * 16;
+        vp = vv8 + ((unit_row0 + key) * D) * 2 + cc * 16;
+      }
+      lds_dma16(kp, kl + (r * kWaves + wave) * 1024);
+      lds_dma16(vp, vl + (r * kWaves + wave) * 1024);
+    }
+  };
+  // once tile u has landed: each lane converts the V chunks it loaded to f16 in
+  // place (or zero-fills both chunks of an unreadable page).  Split in a read,
+  // issued before the current tile's math, and a write after it, so the LDS
+  // read latency hides behind the math.
+  auto vread = [&](int u, u32x4 (&vr)[ROUNDS]) __attribute__((always_inline)) {
+    const int sl = u % kDepth;
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r)
+      vr[r] = *reinterpret_cast<const u32x4*>(smem + (kDepth + sl) * TILE + ((r * kWaves + wave) * 64 + lane) * 16);
+  };
+  auto vwrite = [&](int u, const u32x4 (&vr)[ROUNDS]) __attribute__((always_inline)) {
+    const int sl = u % kDepth;
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+      const int s = (r * kWaves + wave) * 64 + lane;
+      u32x4* vc = reinterpret_cast<u32x4*>(smem + (kDepth + sl) * TILE + s * 16);
+      if (PAGED && (zfill >> (sl * ROUNDS + r)) & 1u) {
+        *vc = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(smem + sl * TILE + s * 16) = u32x4{0u, 0u, 0u, 0u};
+      } else {
+        *vc = bf16x8_to_f16x8(vr[r]);
       }
     }
   };
-  auto store_tile = [&](int buf, int set) {
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int c = threadIdx.x + u * kThreads;
-      if (c < CH) {
-        const int kk = c / (D / 8), c8 = c % (D / 8);
-        *reinterpret_cast<u32x4*>(&Ks[buf][kk * KP + c8 * 8]) = kreg[set][u];
-        *reinterpret_cast<u32x4*>(&Vs[buf][kk * VP + c8 * 8]) = bf16x8_to_f16x8(vreg[set][u]);
-      }
-    }
+  // wait until tile u's loads have landed, given the last tile issued so far
+  auto wait_tile = [&](int u, int last_issued) __attribute__((always_inline)) {
+    const int after = last_issued - u;  // tiles issued after u
+    if (after >= 2) wait_vmem<2 * NDMA>();
+    else if (after == 1) wait_vmem<NDMA>();
+    else wait_vmem<0>();
   };
 
-  // tile t sits in register set t & 1 until it is stored to LDS buffer t & 1 at
-  // the start of iteration t - 1; its loads were issued in iteration t - 3.
   const int ntiles = ke > kb ? (ke - kb + kKT - 1) / kKT : 0;
+  static_assert(kDepth == 4, "wait_tile covers up to 2 tiles in flight behind the one awaited");
   if (ntiles > 0) {
-    load_tile(kb, 0);
-    store_tile(0, 0);
-    if (ntiles > 1) load_tile(kb + kKT, 1);
-    if (ntiles > 2) load_tile(kb + 2 * kKT, 0);
+#pragma unroll
+    for (int u = 0; u < kDepth - 1; ++u)
+      if (u < ntiles) issue(u);
+    wait_tile(0, min(ntiles - 1, kDepth - 2));
+    u32x4 vr[ROUNDS];
+    vread(0, vr);
+    vwrite(0, vr);
   }
   __syncthreads();
-  // one tile; `buf` is a literal at each call so register sets index statically
-  auto step = [&](int t, const int buf) __attribute__((always_inline)) {
+  for (int t = 0; t < ntiles; ++t) {
     const int t0 = kb + t * kKT;
-    if (t + 1 < ntiles) store_tile(buf ^ 1, buf ^ 1);  // LDS buffer read before the last barrier
-    if (t + 3 < ntiles) load_tile(t0 + 3 * kKT, buf ^ 1);
+    // ring slot (t + 3) % 4 was last read in step t - 1, which ended with a barrier
+    if (t + kDepth - 1 < ntiles) {
+      wait_lds_reads();
+      issue(t + kDepth - 1);
+    }
+    // tile t + 1: its loads (issued two steps ago) must have landed; read its V
+    // chunks now, convert and write them after this tile's math
+    u32x4 vnext[ROUNDS];
+    const bool has_next = t + 1 < ntiles;
+    if (has_next) {
+      wait_tile(t + 1, min(ntiles - 1, t + kDepth - 1));
+      vread(t + 1, vnext);
+    }
+    const unsigned char* kt = smem + (t % kDepth) * TILE;
+    const unsigned char* vt = smem + (kDepth + t % kDepth) * TILE;
     if (wave_live) {
       // scores for every query tile; K operands read once, shared by the tiles
       f32x4 s[MT][2];
@@ -198,10 +244,11 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
       for (int i = 0; i < MT; ++i) s[i][0] = s[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
+        const int row = 16 * h + col;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-          const bf16x8 ka =
-              *reinterpret_cast<const bf16x8*>(&Ks[buf][(16 * h + col) * KP + quad * (D / 4) + 8 * ks]);
+          const int c = quad * (CPR / 4) + ks;
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + (row * CPR + (c ^ (row % CPR))) * 16);
 #pragma unroll
           for (int i = 0; i < MT; ++i)
             if (i < MT - 1 || last_live) s[i][h] = mfma_bf16(ka, qb[i][ks], s[i][h]);
@@ -261,23 +308,25 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
         }
         l[i] += ps;
       }
-      // P . V: V operands read once per column tile, shared by the query tiles
+      // P . V: V operands read once per column tile (transposed), shared by the query tiles
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        const uint16_t* base = &Vs[buf][16 * ct + 4 * (col & 3)];
-        const s16x4 lo4 = lds_read_tr16(base + (4 * quad + (col >> 2)) * VP);
-        const s16x4 hi4 = lds_read_tr16(base + (16 + 4 * quad + (col >> 2)) * VP);
+        const int c = 2 * ct + ((col & 3) >> 1);
+        const int r0 = 4 * quad + (col >> 2), r1 = r0 + 16;
+        const uint16_t* p0 =
+            reinterpret_cast<const uint16_t*>(vt + (r0 * CPR + (c ^ (r0 % CPR))) * 16 + 8 * (col & 1));
+        const uint16_t* p1 =
+            reinterpret_cast<const uint16_t*>(vt + (r1 * CPR + (c ^ (r1 % CPR))) * 16 + 8 * (col & 1));
+        const s16x4 lo4 = lds_read_tr16(p0);
+        const s16x4 hi4 = lds_read_tr16(p1);
         const f16x8 bv = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int i = 0; i < MT; ++i)
           if (i < MT - 1 || last_live) O[i][ct] = mfma_f16(A[i], bv, O[i][ct]);
       }
     }
+    if (has_next) vwrite(t + 1, vnext);
     __syncthreads();
-  };
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, 0);
-    if (t + 1 < ntiles) step(t + 1, 1);
   }
 
   // finalise: the row sum over the 4 lanes of a column, then write o (or the

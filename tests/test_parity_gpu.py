@@ -140,6 +140,38 @@ def test_verify_parity(w):
             assert_close(got[b, h * g:(h + 1) * g], ref, f"{w.name} b{b} h{h}")
 
 
+def test_verify_paged_unreadable_slots_read_as_zeros():
+    """A page-table slot outside [0, n_slots) reads as zero rows (include/vc.h,
+    vc_kv_full): the oracle sees those pages' K and V rows as zeros."""
+    from compressed_kv_draft_amd.workload import DeviceWorkload
+    print("[case] verify paged, unreadable slots", flush=True)
+    w = C.TINY.with_(name="v_paged_bad", B=2, Hq=8, Hkv=2, D=128, L=320, k=7, paged=True, page_tokens=16,
+                     seed=46, kind="identity")
+    dw = DeviceWorkload(w, with_vocab=False)
+    n_slots = int(dw.full.desc.n_slots)
+    bad = {(0, 1): -1, (1, 3): n_slots + 5, (1, 0): -7, (0, 20): n_slots}  # page 20 holds the drafted rows
+    for (b, p), v in bad.items():
+        dw.page_table[b, p] = v
+    got = dw.verify().cpu().numpy()
+    pt, g = w.page_tokens, w.g
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            K, V = dw.np["K"][b, h][:w.L].copy(), dw.np["V"][b, h][:w.L].copy()
+            Kn, Vn = dw.np["Kn"][b, h].copy(), dw.np["Vn"][b, h].copy()
+            for (bb, p) in bad:
+                if bb != b:
+                    continue
+                for r in range(p * pt, (p + 1) * pt):
+                    if r < w.L:
+                        K[r] = 0
+                        V[r] = 0
+                    elif r < w.L + w.n_q:
+                        Kn[r - w.L] = 0
+                        Vn[r - w.L] = 0
+            ref = R.unit_verify(w, K, V, Kn, Vn, dw.np["Q"][b, h * g:(h + 1) * g])
+            assert_close(got[b, h * g:(h + 1) * g], ref, f"paged bad slots b{b} h{h}")
+
+
 def test_verify_prefill_causal():
     """ctx_len = 0 and many positions: plain causal self-attention (prefill)."""
     import torch
