@@ -24,8 +24,9 @@
 //
 // Work split: a workgroup (4 wavefronts) owns one (batch, kv-head) and a range
 // of 32-token blocks; wavefronts take every 4th block and keep their own
-// online-softmax state, merged in LDS at the end.  Workgroups past the main
-// splits handle the exact tail.  draft_combine_kernel merges the splits.
+// online-softmax state, merged in LDS at the end.  The last workgroups of each
+// (batch, kv-head) first take a range of the exact tail rows as a partial of
+// their own.  draft_combine_kernel merges the partials.
 #include <map>
 #include <mutex>
 
@@ -57,9 +58,11 @@ struct DraftArgs {
   float* lse;
   int B, Hq, Hkv, g;
   float scale_log2;
-  int main_splits, main_bpw;  // workgroups for the compressed part, blocks per workgroup
-  int tail_bpw;               // blocks per tail workgroup
-  int splits;                 // all workgroups of one (batch, kv-head)
+  int main_splits;            // workgroups of one (batch, kv-head)
+  int main_bpw, main_bpw_t;   // compressed blocks per workgroup: before / from tail_first
+  int tail_first, tail_bpw;   // workgroups >= tail_first first take tail_bpw exact tail blocks
+  int splits;                 // partials per (batch, kv-head): main_splits + tail workgroups
+  int direct;                 // 1: a single partial, written as the output
   float* ws;                  // split partials [splits][B][Hq][D + 2]
 };
 
@@ -357,13 +360,129 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) st.O[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const bool is_tail = split >= a.main_splits;
   const size_t unit_rows = (size_t)unit;
 
-  if (!is_tail) {
+  // Merge the wavefronts' states through LDS and write partial `part` (or the
+  // output).  quant: the state holds the compressed part's code-scaled,
+  // slot-grouped P.V (else exact-row P.V with hi/lo rows).
+  auto finish = [&](int part, bool quant) __attribute__((always_inline)) {
+    float lt = st.l;
+    lt += shfl_xor(lt, 16);
+    lt += shfl_xor(lt, 32);
+    float zt[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      zt[v] = st.zacc[v];
+      zt[v] += shfl_xor(zt[v], 16);
+      zt[v] += shfl_xor(zt[v], 32);
+    }
+    __syncthreads();  // every wavefront is done with its staging region
+    float* s_o = reinterpret_cast<float*>(smem);  // [kWaves][8][D]
+    float* s_m = s_o + kWaves * 8 * D;            // [kWaves][8]
+    float* s_l = s_m + kWaves * 8;                // [kWaves][8]
+    float* s_z = s_l + kWaves * 8;                // [kWaves][8][4]
+    const bool quant_wg = BITS > 0 && quant;
+    if (quad == 0 && rep == 0 && hilo == 0) {
+      s_m[wave * 8 + head] = st.m;
+      s_l[wave * 8 + head] = lt;
+      if (!quant_wg) {
+#pragma unroll
+        for (int G = 0; G < NG; ++G) s_z[(wave * 8 + head) * 4 + G] = 0.0f;
+      }
+    }
+    if (quant_wg && quad == 0 && slot_ok) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const int G = slot + v * SP;
+        if (G < NG) s_z[(wave * 8 + head) * 4 + G] = zt[v];
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      if (quant_wg) {
+        constexpr int B2 = BITS > 0 ? BITS : 2;
+        const float osc = __builtin_ldexpf(1.0f, 24 - B2 * code_target<B2, Cfg<D, B2>::VWIDE>(ct % Cfg<D, B2>::PPD));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * quad + i;
+          const int hp_ = r >> 1, rep_ = hp_ / g;
+          const int slot_ = 2 * rep_ + (r & 1);
+          if (rep_ < R8 && (ct / 2) % SP == slot_) s_o[(wave * 8 + hp_ % g) * D + 16 * ct + col] = st.O[ct][i] * osc;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const int hp_ = 2 * quad + i / 2;
+          if (hp_ < g) s_o[(wave * 8 + hp_) * D + 16 * ct + col] = st.O[ct][i] + st.O[ct][i + 1];
+        }
+      }
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < g * D; t += kThreads) {
+      const int h = t / D, d = t % D;
+      float M = kNegInf;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w * 8 + h]);
+      float L = 0.0f, O = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = s_m[w * 8 + h];
+        const float f = mw == kNegInf ? 0.0f : fast_exp2(mw - M);
+        L += s_l[w * 8 + h] * f;
+        O += (s_o[(w * 8 + h) * D + d] + s_z[(w * 8 + h) * 4 + d / 32]) * f;
+      }
+      const int hq = hk * g + h;
+      if (a.direct) {
+        a.out[((size_t)b * a.Hq + hq) * D + d] = L > 0.0f ? O / L : 0.0f;
+        if (a.lse != nullptr && d == 0) a.lse[(size_t)b * a.Hq + hq] = L > 0.0f ? (M + __log2f(L)) * kLn2 : kNegInf;
+      } else {
+        float* p = a.ws + (((size_t)part * a.B + b) * a.Hq + hq) * (D + 2);
+        p[d] = O;
+        if (d == 0) {
+          p[D] = M;
+          p[D + 1] = L;
+        }
+      }
+    }
+  };
+  auto reset = [&]() __attribute__((always_inline)) {
+    st.m = kNegInf;
+    st.l = 0.0f;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) st.zacc[v] = 0.0f;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) st.O[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  // ---------------------------------------------------------- exact tail
+  // (the last workgroups first take a range of the exact rows, as a partial
+  // of their own, then a correspondingly smaller range of the compressed part)
+  if (split >= a.tail_first && a.T_cap > 0) {
+    int tl = a.T_cap > 0 ? a.tail_len[b] : 0;
+    tl = tl < 0 ? 0 : (tl > a.T_cap ? a.T_cap : tl);
+    RowSrc src;
+    src.k = a.tail_k;
+    src.v = a.tail_v;
+    src.idx = nullptr;
+    src.unit_row0 = unit_rows * a.T_cap;
+    src.n_valid = tl;
+    src.bound = a.T_cap;
+    const int nb = (tl + 31) / 32;
+    const int blo = (split - a.tail_first) * a.tail_bpw;
+    const int bhi = min(blo + a.tail_bpw, nb);
+    for (int blk = blo + wave; blk < bhi; blk += kWaves)
+      rows_block<D, NV>(src, blk, qb, a.scale_log2, vst, st, lane, col, quad, hilo);
+    finish(a.main_splits + split - a.tail_first, false);
+    reset();
+    __syncthreads();  // the epilogue's LDS is reused below
+  }
+
+  {
+    // ------------------------------------------------ the compressed part
     const int nb = (a.n_main + 31) / 32;
-    const int blo = split * a.main_bpw;
-    const int bhi = min(blo + a.main_bpw, nb);
+    const int before = min(split, a.tail_first);
+    const int blo = before * a.main_bpw + (split - before) * a.main_bpw_t;
+    const int bhi = min(blo + (split < a.tail_first ? a.main_bpw : a.main_bpw_t), nb);
     if constexpr (BITS > 0) {
       // ---------------------------------------------------------------- quant
       // q scaled per k slot (f16, exact): qF = q 2^(kQExp - bits*jj).  The zero-
@@ -551,103 +670,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
       for (int blk = blo + wave; blk < bhi; blk += kWaves)
         rows_block<D, NV>(src, blk, qb, a.scale_log2, vst, st, lane, col, quad, hilo);
     }
-  } else {
-    // -------------------------------------------------------------- exact tail
-    int tl = a.T_cap > 0 ? a.tail_len[b] : 0;
-    tl = tl < 0 ? 0 : (tl > a.T_cap ? a.T_cap : tl);
-    RowSrc src;
-    src.k = a.tail_k;
-    src.v = a.tail_v;
-    src.idx = nullptr;
-    src.unit_row0 = unit_rows * a.T_cap;
-    src.n_valid = tl;
-    src.bound = a.T_cap;
-    const int nb = (tl + 31) / 32;
-    const int blo = (split - a.main_splits) * a.tail_bpw;
-    const int bhi = min(blo + a.tail_bpw, nb);
-    for (int blk = blo + wave; blk < bhi; blk += kWaves)
-      rows_block<D, NV>(src, blk, qb, a.scale_log2, vst, st, lane, col, quad, hilo);
   }
-
-  // ------------------------------------------------------------------ epilogue
-  float lt = st.l;
-  lt += shfl_xor(lt, 16);
-  lt += shfl_xor(lt, 32);
-  float zt[NV];
-#pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    zt[v] = st.zacc[v];
-    zt[v] += shfl_xor(zt[v], 16);
-    zt[v] += shfl_xor(zt[v], 32);
-  }
-  __syncthreads();  // every wavefront is done with its staging region
-  float* s_o = reinterpret_cast<float*>(smem);  // [kWaves][8][D]
-  float* s_m = s_o + kWaves * 8 * D;            // [kWaves][8]
-  float* s_l = s_m + kWaves * 8;                // [kWaves][8]
-  float* s_z = s_l + kWaves * 8;                // [kWaves][8][4]
-  const bool quant_wg = BITS > 0 && !is_tail;
-  if (quad == 0 && rep == 0 && hilo == 0) {
-    s_m[wave * 8 + head] = st.m;
-    s_l[wave * 8 + head] = lt;
-    if (!quant_wg) {
-#pragma unroll
-      for (int G = 0; G < NG; ++G) s_z[(wave * 8 + head) * 4 + G] = 0.0f;
-    }
-  }
-  if (quant_wg && quad == 0 && slot_ok) {
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      const int G = slot + v * SP;
-      if (G < NG) s_z[(wave * 8 + head) * 4 + G] = zt[v];
-    }
-  }
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    if (quant_wg) {
-      constexpr int B2 = BITS > 0 ? BITS : 2;
-      const float osc = __builtin_ldexpf(1.0f, 24 - B2 * code_target<B2, Cfg<D, B2>::VWIDE>(ct % Cfg<D, B2>::PPD));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * quad + i;
-        const int hp_ = r >> 1, rep_ = hp_ / g;
-        const int slot_ = 2 * rep_ + (r & 1);
-        if (rep_ < R8 && (ct / 2) % SP == slot_) s_o[(wave * 8 + hp_ % g) * D + 16 * ct + col] = st.O[ct][i] * osc;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; i += 2) {
-        const int hp_ = 2 * quad + i / 2;
-        if (hp_ < g) s_o[(wave * 8 + hp_) * D + 16 * ct + col] = st.O[ct][i] + st.O[ct][i + 1];
-      }
-    }
-  }
-  __syncthreads();
-  for (int t = threadIdx.x; t < g * D; t += kThreads) {
-    const int h = t / D, d = t % D;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w * 8 + h]);
-    float L = 0.0f, O = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = s_m[w * 8 + h];
-      const float f = mw == kNegInf ? 0.0f : fast_exp2(mw - M);
-      L += s_l[w * 8 + h] * f;
-      O += (s_o[(w * 8 + h) * D + d] + s_z[(w * 8 + h) * 4 + d / 32]) * f;
-    }
-    const int hq = hk * g + h;
-    if (a.splits == 1) {
-      a.out[((size_t)b * a.Hq + hq) * D + d] = L > 0.0f ? O / L : 0.0f;
-      if (a.lse != nullptr && d == 0) a.lse[(size_t)b * a.Hq + hq] = L > 0.0f ? (M + __log2f(L)) * kLn2 : kNegInf;
-    } else {
-      float* p = a.ws + (((size_t)split * a.B + b) * a.Hq + hq) * (D + 2);
-      p[d] = O;
-      if (d == 0) {
-        p[D] = M;
-        p[D + 1] = L;
-      }
-    }
-  }
+  finish(split, true);
 }
 
 // Merge the split partials (o unnormalised, m in log2 units, l) of one (b, h)
@@ -701,32 +725,42 @@ size_t draft_ws_need(int B, int Hq, int Hkv, int D, int splits) {
 }
 
 struct DraftPlan {
-  int main_splits, main_bpw, tail_splits, tail_bpw, splits;
+  int main_splits, main_bpw, main_bpw_t, tail_first, tail_bpw, splits;
 };
 
-constexpr int kTailBpw = 2 * kWaves;  // tail workgroups: up to 2 blocks per wavefront
+constexpr int kTailBpw = 2 * kWaves;  // exact tail blocks per workgroup: up to 2 per wavefront
 
-// wgs_per_cu: resident workgroups per CU of the kernel that will run.  The
-// tail workgroups are placed first; the main part takes the remaining resident
-// slots, so that every workgroup of the grid starts at once.
-DraftPlan plan_draft(int units, int main_blocks, int tail_blocks, int wgs_per_cu) {
+// Time of one exact-row block (bf16, loaded straight to registers, latency-
+// bound when taken alone) per wavefront, in quarters of one block of the
+// compressed part (measured on MI355X: about 3.25 int2 blocks, 2.5 int4 blocks;
+// an exact-row main part costs the same per block).
+inline int tail_block_cost_q4(int bits) { return bits == 2 ? 13 : bits == 4 ? 10 : 4; }
+
+// wgs_per_cu: resident workgroups per CU of the kernel that will run.  Every
+// resident slot runs compressed blocks.  The exact tail goes to the last
+// workgroups of each (batch, kv-head), which take it first, as a partial of its
+// own, and then correspondingly fewer compressed blocks, so that all
+// workgroups finish together.
+DraftPlan plan_draft(int units, int main_blocks, int tail_blocks, int wgs_per_cu, int bits) {
   DraftPlan p{};
-  p.tail_bpw = kTailBpw;
-  p.tail_splits = (tail_blocks + kTailBpw - 1) / kTailBpw;
-  if (main_blocks > 0) {
-    const int target = wgs_per_cu * num_cus() - units * p.tail_splits;
-    int s = target / units;
-    const int cap = (main_blocks + 2 * kWaves - 1) / (2 * kWaves);  // >= 2 blocks per wavefront
-    if (s > cap) s = cap;
-    if (s < 1) s = 1;
-    p.main_bpw = (main_blocks + s - 1) / s;
-    p.main_splits = (main_blocks + p.main_bpw - 1) / p.main_bpw;
-  }
-  p.splits = p.main_splits + p.tail_splits;
-  if (p.splits == 0) {  // no key at all: one empty workgroup writes o = 0
-    p.tail_splits = 1;
-    p.splits = 1;
-  }
+  int s = wgs_per_cu * num_cus() / units;
+  const int cap = (main_blocks + 2 * kWaves - 1) / (2 * kWaves);  // >= 2 blocks per wavefront
+  if (s > cap) s = cap;
+  if (s < 1) s = 1;
+  int t = tail_blocks > 0 ? (tail_blocks + kTailBpw - 1) / kTailBpw : 0;
+  if (t > s) s = t;
+  p.main_splits = s;
+  p.tail_first = s - t;
+  p.tail_bpw = t > 0 ? (tail_blocks + t - 1) / t : 0;
+  // compressed blocks a tail workgroup gives up: the tail's rounds (one block
+  // per wavefront each) times the cost of a round in compressed blocks
+  const int cut = (tail_block_cost_q4(bits) * kWaves * ((p.tail_bpw + kWaves - 1) / kWaves) + 3) / 4;
+  p.main_bpw = (main_blocks + t * cut + s - 1) / s;
+  p.main_bpw_t = p.main_bpw > cut ? p.main_bpw - cut : 0;
+  if (t == 0) p.main_bpw_t = p.main_bpw;
+  // the tail workgroups may have taken less than their share: the others cover the rest
+  while ((long long)p.tail_first * p.main_bpw + (long long)t * p.main_bpw_t < main_blocks) ++p.main_bpw;
+  p.splits = s + t;
   return p;
 }
 
@@ -764,8 +798,9 @@ extern "C" size_t vc_draft_ws_bytes(int B, int Hq, int Hkv, int D, int max_keys)
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_keys < 0) return 0;
   // upper bound over every split of max_keys between the compressed part and the tail
   const int nb = (max_keys + 31) / 32;
-  const DraftPlan p = plan_draft(B * Hkv, nb, 0, 8);  // 8 resident workgroups per CU bound any kernel
-  const int s = p.main_splits + (nb + kTailBpw - 1) / kTailBpw + 1;
+  // (one more tail workgroup than the worst split of max_keys could need)
+  const DraftPlan p = plan_draft(B * Hkv, nb, 0, 8, 0);  // 8 resident workgroups per CU bound any kernel
+  const int s = p.main_splits + 2 * ((nb + kTailBpw - 1) / kTailBpw) + 1;
   return draft_ws_need(B, Hq, Hkv, D, s);
 }
 
@@ -849,7 +884,7 @@ extern "C" int vc_draft_attn(const vc_kv_comp* comp, const vc_tail* tail, const 
   const int nv = bits > 0 && SP < NG ? 2 : 1;
   const DraftKernel kern = D == 128 ? (nv == 2 ? pick_kernel<128, 2>(bits) : pick_kernel<128, 1>(bits))
                                     : pick_kernel<64, 1>(bits);
-  const DraftPlan p = plan_draft(units, main_blocks, tail_blocks, wgs_per_cu(kern));
+  const DraftPlan p = plan_draft(units, main_blocks, tail_blocks, wgs_per_cu(kern), bits);
   VC_CHECK(p.splits <= kMaxCombineSplits, "vc_draft_attn: %d splits exceed %d", p.splits, kMaxCombineSplits);
   const size_t need = draft_ws_need(B, Hq, Hkv, D, p.splits);
   if (p.splits > 1) {
@@ -860,9 +895,12 @@ extern "C" int vc_draft_attn(const vc_kv_comp* comp, const vc_tail* tail, const 
   }
   a.main_splits = p.main_splits;
   a.main_bpw = p.main_bpw;
+  a.main_bpw_t = p.main_bpw_t;
+  a.tail_first = p.tail_first;
   a.tail_bpw = p.tail_bpw;
   a.splits = p.splits;
-  dim3 grid(p.splits, units);
+  a.direct = p.splits == 1;
+  dim3 grid(p.main_splits, units);
   kern<<<grid, kThreads, 0, stream>>>(a);
   VC_HIP(hipGetLastError());
   if (p.splits > 1) {
