@@ -174,7 +174,7 @@ def kernel_source_digest():
     """sha256 of the draft kernel's sources: ties a stored counter reading to the code it was taken on."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("draft.hip", "mfma.h", "vc_common.h"):
+    for f in ("draft.hip", "lds_dma.h", "mfma.h", "vc_common.h"):
         with open(os.path.join(ROOT, "compressed_kv_draft_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
