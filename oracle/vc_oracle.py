@@ -256,14 +256,14 @@ def verify_attention_unit(q: np.ndarray, k_all: np.ndarray, v_all: np.ndarray, L
     Written as one masked batch, a different code path from the decode step."""
     g, nq, D = q.shape
     n = L + nq
-    s = np.einsum("hjd,td->hjt", q, k_all[:n]) * scale           # [g, n_q, n]
+    s = np.matmul(q, k_all[:n].T) * scale                         # [g, n_q, n]
     tok = np.arange(n)[None, None, :]
     lim = (L + np.arange(nq))[None, :, None]
     s = np.where(tok <= lim, s, -np.inf)
     s = s - s.max(axis=2, keepdims=True)
     p = np.exp(s)
     p = p / p.sum(axis=2, keepdims=True)
-    return np.einsum("hjt,td->hjd", p, v_all[:n])
+    return np.matmul(p, v_all[:n])
 
 
 # ----------------------------------------------------------------------------
