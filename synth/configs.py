@@ -63,3 +63,55 @@ LLAMA70B = Workload("llama_70b_layer_b16_l64k_int4_paged_k32", B=16, Hq=64, Hkv=
                     groups=2, chunk_tokens=4096, seed=4)
 
 ALL = {w.name: w for w in (TINY, LLAMA8B, QWEN32B, LLAMA70B)}
+
+
+@dataclass(frozen=True)
+class TinyLM:
+    """A small Llama-style decoder run end to end through the draft-then-verify loop.
+
+    Architecture (the pages name none): pre-norm blocks of RMSNorm -> Q/K/V
+    projections -> rotary positions -> GQA attention -> output projection ->
+    residual, then RMSNorm -> SwiGLU feed-forward -> residual; a final RMSNorm
+    and an untied vocabulary head.  Weight matrices are stored [in, out]."""
+    name: str
+    n_layers: int
+    d_model: int
+    Hq: int
+    Hkv: int
+    D: int
+    ffn: int
+    vocab: int
+    prompt: int       # prompt tokens (all quantised for the draft cache)
+    k: int            # draft length
+    n_gen: int        # generated tokens
+    bits: int = 4
+    q_gain: float = 1.0   # W_q std multiplier: sharpens attention so that the lossy draft matters
+    plant: float = 0.0    # successor-plant strength (logit units) added to the vocabulary head
+    rope_theta: float = 10000.0
+    eps: float = 1e-5
+    seed: int = 5
+
+    @property
+    def g(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def L_cap(self) -> int:
+        """Rows of the full cache: prompt + generated + one round of drafts, rounded up to 64."""
+        n = self.prompt + self.n_gen + self.k + 1
+        return (n + 63) // 64 * 64
+
+    @property
+    def T_cap(self) -> int:
+        """Rows of the draft's exact tail: generated rows plus one round of drafts, rounded up to 32."""
+        n = self.n_gen + self.k + 1
+        return (n + 31) // 32 * 32
+
+    def with_(self, **kw) -> "TinyLM":
+        return replace(self, **kw)
+
+
+LM_E2E = TinyLM("tiny_lm_4l_d1024_p16k_int4_k32_g256", n_layers=4, d_model=1024, Hq=16, Hkv=4, D=64,
+                ffn=2816, vocab=32000, prompt=16384, k=32, n_gen=256, bits=4, q_gain=3.0, plant=12.0, seed=5)
+LM_SMALL = TinyLM("small_lm_2l_d256_p256_int4_k8_g40", n_layers=2, d_model=256, Hq=4, Hkv=2, D=64,
+                  ffn=512, vocab=2048, prompt=256, k=8, n_gen=40, bits=4, q_gain=1.0, plant=6.0, seed=15)
