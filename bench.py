@@ -34,6 +34,11 @@ def parse():
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain 1 GiB device-to-device copy, 3 times (the reference kernel for "
                         "scaling the FETCH_SIZE / WRITE_SIZE counters to bytes)")
+    p.add_argument("--steps-e2e", type=int, default=3)
+    p.add_argument("--warmup-e2e", type=int, default=1)
+    p.add_argument("--e2e", action="store_true",
+                   help="end-to-end draft-then-verify generation with the tiny decoder (256 tokens, int4 draft, "
+                        "k = 32): verified tokens/s and the acceptance histogram instead of the per-layer line")
     p.add_argument("--stagger", action="store_true",
                    help="measure the full-KV prefetch of one request group against the other group's drafting "
                         "(Llama-70B-shaped paged workload) and print that JSON line instead")
@@ -234,6 +239,85 @@ def cpu_baseline(w, dw, n_accept_sum, units):
                       f"fp64 numpy, {dt:.1f} s measured, scaled x{(w.B * w.Hkv) / len(picks):.0f}"}
 
 
+def e2e(a):
+    """Tiny decoder end to end: prefill, then 256 greedy tokens by the loop.
+    Every attention and token decision runs in libvc; the dense layers are
+    torch fp32.  Reports decode tokens/s (prefill excluded), the accepted-count
+    histogram, and whether the tokens equal the stored oracle sequence."""
+    import numpy as np
+    import torch
+
+    from compressed_kv_draft_amd.tinylm import TinyLM
+    from synth import configs as C
+    from synth import model as M
+    cfg = C.LM_E2E
+    W = M.weights(cfg)
+    cos, sin = M.rope_tables(cfg)
+    prompt = M.prompt(cfg)
+    runs = []
+    for i in range(a.warmup_e2e + a.steps_e2e):
+        lm = TinyLM(cfg, W, cos, sin)
+        toks, acc, st = lm.generate(prompt, cfg.n_gen)
+        if i >= a.warmup_e2e:
+            runs.append((toks, acc, st))
+        del lm
+        torch.cuda.empty_cache()
+    gold = None
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tests", "golden", f"e2e_{cfg.name}.txt")
+    if os.path.exists(path):
+        for line in open(path):
+            if line.startswith("tokens="):
+                gold = [int(x) for x in line.split("=", 1)[1].split()]
+    dec = [r[2]["decode_s"] for r in runs]
+    toks, acc, st = runs[int(np.argmin(dec))]
+    hist = {str(k): int(v) for k, v in zip(*np.unique(acc, return_counts=True))}
+    line = {"metric": "end-to-end verified tokens/s (tiny decoder, draft-then-verify, greedy)",
+            "value": round((cfg.n_gen - 1) / min(dec), 1), "unit": "tokens/s", "n_gpus": 1,
+            "steps": a.steps_e2e, "warmup": a.warmup_e2e, "higher_is_better": True, "data": "synthetic",
+            "config": {"workload": cfg.name, "layers": cfg.n_layers, "d_model": cfg.d_model, "q_heads": cfg.Hq,
+                       "kv_heads": cfg.Hkv, "head_dim": cfg.D, "ffn": cfg.ffn, "vocab": cfg.vocab,
+                       "prompt": cfg.prompt, "draft_len": cfg.k, "generated": cfg.n_gen, "draft_cache": "int4",
+                       "dense_layers": "torch fp32 (outside the measured path)"},
+            "rounds": st["rounds"], "accepted_per_round": acc, "accepted_histogram": hist,
+            "mean_tokens_per_round": round(float(np.mean(np.array(acc) + 1)), 2),
+            "decode_s": [round(x, 4) for x in dec], "prefill_s": round(st["prefill_s"], 4),
+            "equals_oracle_greedy": (toks == gold) if gold is not None else None}
+    print(json.dumps(line), flush=True)
+
+
+def full_kv_decode(w, dw, value, step_s, launches=20):
+    """Baseline without drafting: one decode step reads the whole bf16 cache
+    (vc_draft_attn with the identity compressor over the L context rows plus the
+    current row) and yields one token per sequence.  Returns its timing and
+    tokens/s, and the speed-up of the draft-then-verify step over it."""
+    import torch
+
+    import compressed_kv_draft_amd as vc
+    dev = dw.full_k.device
+    ident = vc.identity_cache(dw.full_k, dw.full_v, w.L + 1)
+    no_tail = vc.Tail()
+    ws = torch.zeros(vc.draft_ws_bytes(w.B, w.Hq, w.Hkv, w.D, w.L + 1), dtype=torch.uint8, device=dev)
+    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
+    q = dw.q_steps[0]
+    stream = torch.cuda.current_stream()
+    for _ in range(10):
+        vc.draft_attn(ident, no_tail, q, dw.scale, out=out, ws=ws, Hkv=w.Hkv)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(launches):
+        vc.draft_attn(ident, no_tail, q, dw.scale, out=out, ws=ws, Hkv=w.Hkv)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / launches
+    nbytes = w.B * w.Hkv * (w.L + 1) * w.D * 2 * 2
+    tps = w.B / t
+    return {"avg_us": round(1e6 * t, 2), "bytes": nbytes, "GBps": round(nbytes / t / 1e9, 1),
+            "tokens_per_s": round(tps, 1), "speedup_at_measured_n": round(value / tps, 3),
+            "speedup_at_n_eq_k": round(w.B * w.n_q / step_s / tps, 3),
+            "speedup_at_n_eq_25": round(w.B * 26 / step_s / tps, 3)}
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -245,6 +329,9 @@ def main():
         return
     if a.calibrate_copy:
         calibrate_copy()
+        return
+    if a.e2e:
+        e2e(a)
         return
     import numpy as np
     import torch
@@ -347,6 +434,7 @@ def main():
                    "ms_per_step": round(verify_total, 4)},
         "roofline": roof,
     }
+    line["full_kv_decode"] = full_kv_decode(w, dw, value, step_s)
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, dw, int(n.sum()), a.cpu_units)
     print(json.dumps(line), flush=True)

@@ -1,0 +1,200 @@
+"""Greedy generation by the draft-then-verify loop on a small Llama-style decoder.
+
+[VC Core Algorithm] the target model drafts k tokens reading the compressed
+cache, verifies them in one causal pass over the full cache, keeps the
+matching prefix plus one verifier token and repeats from there.
+
+Every attention and every token decision runs in libvc: vc_verify_attn (the
+prefill and each verification pass), vc_quantize_kv (the int4 draft cache of
+the prompt), vc_draft_attn (each draft position), vc_argmax (draft tokens and
+the first token) and vc_accept.  The dense layers, norms and rotary positions
+around them are torch fp32 operations (harness glue, not the measured path).
+
+Model: pre-norm blocks x += O(attn(RMSNorm(x))); x += SwiGLU(RMSNorm(x)); a
+final RMSNorm and the vocabulary head.  q, and the k/v rows written to the
+caches, are rounded to bf16 after the rotary step; attention outputs are fp32.
+Cache bookkeeping per round, with the pending token at position ctx:
+  * draft position j (token x_j at ctx + j) writes its k/v into the draft tail
+    at row (ctx - P) + j and attends to the int4 prompt plus tail rows
+    [0, ctx - P + j]; the tail's first ctx - P rows are the verified rows of
+    earlier rounds;
+  * verification writes the k/v of positions ctx .. ctx + k into the full cache
+    and attends causally; after acceptance of n drafts, rows ctx .. ctx + n
+    are copied into the tail (the draft's own rows there are overwritten) and
+    the rows after them are left to be rewritten by the next round.
+"""
+from __future__ import annotations
+
+import time
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+from . import _lib as vc
+
+
+def _bf16_to_f32(bits: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16).float()
+
+
+class TinyLM:
+    def __init__(self, cfg, W: dict, cos: np.ndarray, sin: np.ndarray, device="cuda"):
+        torch.backends.cuda.matmul.allow_tf32 = False
+        self.cfg, self.dev = cfg, device
+        c = cfg
+        f = lambda b: _bf16_to_f32(b, device)  # noqa: E731
+        self.embed = f(W["embed"])
+        self.layers = [{n: f(W[n][l]) for n in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down",
+                                                   "attn_norm", "ffn_norm")} for l in range(c.n_layers)]
+        self.final_norm = f(W["final_norm"])
+        self.head = f(W["lm_head"])
+        self.cos = torch.from_numpy(np.ascontiguousarray(cos)).to(device)
+        self.sin = torch.from_numpy(np.ascontiguousarray(sin)).to(device)
+        self.scale = float(np.float32(1.0 / np.sqrt(c.D)))
+        bf = dict(dtype=torch.bfloat16, device=device)
+        self.K = [torch.zeros((1, c.Hkv, c.L_cap, c.D), **bf) for _ in range(c.n_layers)]
+        self.V = [torch.zeros((1, c.Hkv, c.L_cap, c.D), **bf) for _ in range(c.n_layers)]
+        self.full = [vc.FullKV(self.K[l], self.V[l], L_cap=c.L_cap) for l in range(c.n_layers)]
+        self.TK = [torch.zeros((1, c.Hkv, c.T_cap, c.D), **bf) for _ in range(c.n_layers)]
+        self.TV = [torch.zeros((1, c.Hkv, c.T_cap, c.D), **bf) for _ in range(c.n_layers)]
+        self.tail_len = torch.zeros(1, dtype=torch.int32, device=device)
+        self.tails = [vc.Tail(self.TK[l], self.TV[l], self.tail_len) for l in range(c.n_layers)]
+        self.ctx_t = torch.zeros(1, dtype=torch.int32, device=device)
+        self.comp = None
+        self.draft_ws = None
+        self.verify_ws = torch.empty(
+            vc.verify_ws_bytes(1, c.Hq, c.Hkv, c.D, c.k + 1, c.L_cap - (c.k + 1)), dtype=torch.uint8, device=device)
+        self.q_out = torch.empty((1, c.Hq, c.D), dtype=torch.float32, device=device)
+
+    # ------------------------------------------------------------ dense glue
+
+    def _rms(self, x, gain):
+        return x * torch.rsqrt(x.pow(2).mean(-1, keepdim=True) + self.cfg.eps) * gain
+
+    def _rope(self, x, pos):
+        """x [n, H, D] fp32, pos int64 [n]: rotate channel pairs (i, i + D/2)."""
+        half = self.cfg.D // 2
+        cs, sn = self.cos[pos][:, None, :], self.sin[pos][:, None, :]
+        a, b = x[..., :half], x[..., half:]
+        return torch.cat([a * cs - b * sn, b * cs + a * sn], dim=-1)
+
+    def _project(self, l, x, pos):
+        """x [n, d] -> q bf16 [1, Hq, n, D]; k, v bf16 [Hkv, n, D]."""
+        c, P = self.cfg, self.layers[l]
+        n = x.shape[0]
+        a = self._rms(x, P["attn_norm"])
+        q = self._rope((a @ P["wq"]).view(n, c.Hq, c.D), pos)
+        k = self._rope((a @ P["wk"]).view(n, c.Hkv, c.D), pos)
+        v = (a @ P["wv"]).view(n, c.Hkv, c.D)
+        q = q.to(torch.bfloat16).transpose(0, 1).contiguous().unsqueeze(0)
+        return q, k.to(torch.bfloat16).transpose(0, 1), v.to(torch.bfloat16).transpose(0, 1)
+
+    def _finish(self, l, x, o):
+        """x [n, d]; o fp32 [Hq, n, D]."""
+        c, P = self.cfg, self.layers[l]
+        n = x.shape[0]
+        x = x + o.transpose(0, 1).reshape(n, c.Hq * c.D) @ P["wo"]
+        a = self._rms(x, P["ffn_norm"])
+        return x + (F.silu(a @ P["w_gate"]) * (a @ P["w_up"])) @ P["w_down"]
+
+    def _logits(self, x):
+        return self._rms(x, self.final_norm) @ self.head
+
+    # ------------------------------------------------------------ passes
+
+    def causal_pass(self, ids: torch.Tensor, start: int) -> torch.Tensor:
+        """Positions start .. start + n - 1 through every layer in one causal
+        pass over the full cache (vc_verify_attn); returns final hidden [n, d]."""
+        c = self.cfg
+        n = ids.shape[0]
+        pos = torch.arange(start, start + n, device=self.dev)
+        x = self.embed[ids.long()]
+        self.ctx_t.fill_(start)
+        ws = self.verify_ws
+        need = vc.verify_ws_bytes(1, c.Hq, c.Hkv, c.D, n, start)
+        if need > ws.numel():
+            ws = torch.empty(need, dtype=torch.uint8, device=self.dev)
+        for l in range(c.n_layers):
+            q, k, v = self._project(l, x, pos)
+            self.K[l][0, :, start:start + n] = k
+            self.V[l][0, :, start:start + n] = v
+            o = vc.verify_attn(q, self.full[l], self.ctx_t, start, c.Hkv, self.scale, ws=ws)
+            x = self._finish(l, x, o[0])
+        return x
+
+    def prefill(self, prompt: torch.Tensor) -> torch.Tensor:
+        """Full-cache prefill, then the int4 draft cache of every layer.  Returns
+        the last prompt position's logits [V]."""
+        c = self.cfg
+        P = prompt.shape[0]
+        x = self.causal_pass(prompt, 0)
+        self.comp = [vc.quantize_kv(self.K[l], self.V[l], c.bits, P) for l in range(c.n_layers)]
+        self.draft_ws = torch.zeros(vc.draft_ws_bytes(1, c.Hq, c.Hkv, c.D, P + c.T_cap), dtype=torch.uint8,
+                                    device=self.dev)
+        return self._logits(x[-1:])[0]
+
+    def draft_step(self, tok: torch.Tensor, pos: int, row: int) -> torch.Tensor:
+        """One draft position (token tok, int32 [1] on the device) at position
+        pos, writing its tail row `row`; returns its logits [1, V]."""
+        c = self.cfg
+        x = self.embed[tok.long()]
+        p = self._pos(pos)
+        self.tail_len.fill_(row + 1)
+        for l in range(c.n_layers):
+            q, k, v = self._project(l, x, p)
+            self.TK[l][0, :, row] = k[:, 0]
+            self.TV[l][0, :, row] = v[:, 0]
+            o = vc.draft_attn(self.comp[l], self.tails[l], q[:, :, 0].contiguous(), self.scale, out=self.q_out,
+                              ws=self.draft_ws, Hkv=c.Hkv)
+            x = self._finish(l, x, o[0][:, None, :])
+        return self._logits(x)
+
+    def _pos(self, pos: int) -> torch.Tensor:
+        return torch.full((1,), pos, dtype=torch.int64, device=self.dev)
+
+    # ------------------------------------------------------------ the loop
+
+    def generate(self, prompt: np.ndarray, n_gen: int):
+        """Returns (tokens [n_gen] list, per-round accepted counts, stats dict
+        with timings and the logit of every emitted token)."""
+        c = self.cfg
+        P = len(prompt)
+        ids = torch.from_numpy(np.asarray(prompt, dtype=np.int32)).to(self.dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        lg = self.prefill(ids)
+        pending = vc.argmax(lg[None])                       # int32 [1]
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        out = [int(pending.item())]
+        top1 = [float(lg.max().item())]
+        ctx = P
+        accepted = []
+        drafts = torch.empty((1, c.k), dtype=torch.int32, device=self.dev)
+        while len(out) < n_gen:
+            tok = pending
+            for j in range(c.k):
+                lgd = self.draft_step(tok, ctx + j, ctx - P + j)
+                tok = vc.argmax(lgd, ids=drafts[0, j:j + 1])
+            seq = torch.cat([pending, drafts[0]])
+            x = self.causal_pass(seq, ctx)
+            vlog = self._logits(x)
+            emitted, n_acc = vc.accept(drafts, vlog[None])
+            n = int(n_acc.item())
+            em = emitted[0, :n + 1].tolist()
+            out.extend(em)
+            top1.extend(vlog[:n + 1].max(dim=-1).values.tolist())
+            accepted.append(n)
+            r0 = ctx - P
+            for l in range(c.n_layers):
+                self.TK[l][0, :, r0:r0 + n + 1] = self.K[l][0, :, ctx:ctx + n + 1]
+                self.TV[l][0, :, r0:r0 + n + 1] = self.V[l][0, :, ctx:ctx + n + 1]
+            ctx += n + 1
+            pending = emitted[0, n:n + 1].clone()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        out = out[:n_gen]
+        stats = dict(prefill_s=t1 - t0, decode_s=t2 - t1, rounds=len(accepted), top1=top1[:n_gen],
+                     tokens_per_s=(len(out) - 1) / (t2 - t1) if t2 > t1 else 0.0)
+        return out, accepted, stats

@@ -1,0 +1,84 @@
+"""End-to-end draft-then-verify generation on the GPU against the oracle.
+
+[VC Experimental Results] under greedy decoding the loop's output is the one
+the model produces with its full cache.  The tiny decoder at full size (4
+layers, d_model 1024, 16 query / 4 KV heads, head dim 64, 16384-token prompt,
+int4 draft cache, k = 32, 256 tokens) must reproduce the oracle's full-cache
+greedy tokens stored in tests/golden (written by make_e2e_golden.py, which
+calls only oracle/); a smaller decoder is compared with the oracle run live.
+Both runs must also reject at least one draft, so the rollback path runs.
+"""
+import os
+
+import numpy as np
+import pytest
+
+from synth import configs as C
+from synth import model as M
+
+pytestmark = pytest.mark.gpu
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(cfg):
+    kv = {}
+    with open(os.path.join(GOLD, f"e2e_{cfg.name}.txt")) as f:
+        for line in f:
+            if line.startswith("#") or "=" not in line:
+                continue
+            if line.startswith("n_layers="):
+                for item in line.split():
+                    a, b = item.split("=")
+                    kv[a] = b
+                continue
+            a, b = line.rstrip("\n").split("=", 1)
+            kv[a] = b
+    return kv
+
+
+def _run(cfg):
+    from compressed_kv_draft_amd.tinylm import TinyLM
+    W = M.weights(cfg)
+    cos, sin = M.rope_tables(cfg)
+    lm = TinyLM(cfg, W, cos, sin)
+    return lm.generate(M.prompt(cfg), cfg.n_gen)
+
+
+def _compare(cfg, toks, acc, stats, want, want_top1, margins):
+    print(f"  rounds {stats['rounds']} accepted {acc} decode {stats['decode_s']:.3f} s "
+          f"({stats['tokens_per_s']:.0f} tok/s) prefill {stats['prefill_s']:.3f} s", flush=True)
+    n = min(len(toks), len(want))
+    diff = [i for i in range(n) if toks[i] != want[i]]
+    if diff:
+        i = diff[0]
+        pytest.fail(f"{cfg.name}: first mismatch at token {i}: got {toks[i]}, oracle {want[i]} "
+                    f"(oracle margin there {margins[i]:.5f})")
+    assert len(toks) == cfg.n_gen
+    err = np.abs(np.array(stats["top1"]) - np.array(want_top1))
+    print(f"  emitted-token logit |gpu - oracle| max {err.max():.2e}; min oracle margin {min(margins):.4f}",
+          flush=True)
+    assert err.max() < 0.25 * min(margins)
+    assert min(acc) < cfg.k, "no draft rejected: rollback path untested"
+
+
+def test_e2e_tiny_lm_equals_oracle_greedy():
+    cfg = C.LM_E2E
+    g = _golden(cfg)
+    assert g["config"] == cfg.name
+    assert float(g["q_gain"]) == cfg.q_gain and float(g["plant"]) == cfg.plant and int(g["seed"]) == cfg.seed
+    print(f"[case] e2e {cfg.name}", flush=True)
+    toks, acc, stats = _run(cfg)
+    want = [int(x) for x in g["tokens"].split()]
+    _compare(cfg, toks, acc, stats, want, [float(x) for x in g["top1"].split()],
+             [float(x) for x in g["margin"].split()])
+
+
+def test_e2e_small_lm_equals_oracle_greedy():
+    from oracle import e2e as E
+    cfg = C.LM_SMALL
+    print(f"[case] e2e {cfg.name}", flush=True)
+    cos, sin = M.rope_tables(cfg)
+    m = E.Model(cfg, M.weights(cfg), cos, sin)
+    want, top, marg = E.greedy_decode(m, M.prompt(cfg), cfg.n_gen)
+    toks, acc, stats = _run(cfg)
+    _compare(cfg, toks, acc, stats, [int(x) for x in want], list(top), list(marg))
