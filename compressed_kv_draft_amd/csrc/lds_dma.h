@@ -78,6 +78,15 @@ __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Wait for every load the compiler itself has issued so far, through its own
+// s_waitcnt intrinsic (vmcnt 0; expcnt and lgkmcnt left free), so that its
+// wait-insertion pass knows those loads are done.  The pass cannot see the
+// direct loads above: a value it loaded before a loop that issues direct loads
+// and first uses inside it would get its wait inside the loop, where the
+// hardware counter also holds the direct loads, so every iteration would stall
+// until they land.  Call this after such loads and before the loop.
+__device__ __forceinline__ void settle_compiler_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Wait for this wavefront's outstanding LDS reads (before a load may overwrite
 // the LDS they read).
 __device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }

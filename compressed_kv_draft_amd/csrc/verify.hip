@@ -104,7 +104,10 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
   const int tile_end = min(tile0 + a.tiles_per_group, a.NT);
   bf16x8 qb[MT][NKS];
   f32x4 O[MT][NCT];
-  float m[MT], l[MT];
+  // m: running max (log2 units, -inf until a key is seen); mu: the offset the
+  // scores are taken relative to (m, or 0 while m is -inf); thr: the amount a
+  // block max must exceed to move m (-inf while m is -inf, else kTau)
+  float m[MT], l[MT], mu[MT], thr[MT];
   int rlim[MT];
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
@@ -124,8 +127,11 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) O[i][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     m[i] = kNegInf;
+    mu[i] = 0.0f;
+    thr[i] = kNegInf;
     l[i] = 0.0f;
   }
+  settle_compiler_loads();  // q is in registers before the key loop starts
   const bool wave_live = tile0 + wave < tile_end;
   // Only the last query tile needs a liveness guard: a wavefront with any live
   // tile computes its earlier tiles unconditionally.  A dead one has zero
@@ -237,38 +243,40 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
     }
     const unsigned char* kt = smem + (t % kDepth) * TILE;
     const unsigned char* vt = smem + (kDepth + t % kDepth) * TILE;
-    if (wave_live) {
-      // scores for every query tile; K operands read once, shared by the tiles
-      f32x4 s[MT][2];
+    // the tile's math for the first LIVE query tiles of this wavefront (LIVE is
+    // MT, or MT - 1 when the last one is dead): no per-tile guards inside, so
+    // each phase is one straight block the compiler can software-pipeline
+    auto compute = [&](auto live_c) __attribute__((always_inline)) {
+      constexpr int LIVE = decltype(live_c)::value;
+      // scores for every query tile; K operands read once, shared by the tiles,
+      // each read issued one step ahead of its use
+      auto kread = [&](int idx) __attribute__((always_inline)) {
+        const int row = 16 * (idx / NKS) + col, c = quad * (CPR / 4) + idx % NKS;
+        return *reinterpret_cast<const bf16x8*>(kt + (row * CPR + (c ^ (row % CPR))) * 16);
+      };
+      f32x4 s[LIVE][2];
 #pragma unroll
-      for (int i = 0; i < MT; ++i) s[i][0] = s[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < LIVE; ++i) s[i][0] = s[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      bf16x8 kcur = kread(0);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int row = 16 * h + col;
+      for (int idx = 0; idx < 2 * NKS; ++idx) {
+        bf16x8 knext = kcur;
+        if (idx + 1 < 2 * NKS) knext = kread(idx + 1);
+        const int h = idx / NKS, ks = idx % NKS;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const int c = quad * (CPR / 4) + ks;
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + (row * CPR + (c ^ (row % CPR))) * 16);
-#pragma unroll
-          for (int i = 0; i < MT; ++i)
-            if (i < MT - 1 || last_live) s[i][h] = mfma_bf16(ka, qb[i][ks], s[i][h]);
-        }
+        for (int i = 0; i < LIVE; ++i) s[i][h] = mfma_bf16(kcur, qb[i][ks], s[i][h]);
+        kcur = knext;
       }
       // mask only tiles that reach the drafted rows or the end of the range
       const bool need_mask = t0 + kKT > ctx || t0 + kKT > ke;
-      f16x8 A[MT];
+      f16x8 A[LIVE];
 #pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        if (i == MT - 1 && !last_live) {
-          A[i] = f16x8{};
-          continue;
-        }
-        const float mu = m[i] == kNegInf ? 0.0f : m[i];
+      for (int i = 0; i < LIVE; ++i) {
         float xv[8];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) xv[4 * h + e] = fmaf(s[i][h][e], a.scale_log2, -mu);
+          for (int e = 0; e < 4; ++e) xv[4 * h + e] = fmaf(s[i][h][e], a.scale_log2, -mu[i]);
         if (need_mask) {
           // key t0 + 16h + 4q + e is visible iff 16h + e <= lim
           const int lim = min(rlim[i], ke - 1) - t0 - 4 * quad;
@@ -281,11 +289,11 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
         float tl = xv[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) tl = fmaxf(tl, xv[e]);
-        const bool need = m[i] == kNegInf ? tl > kNegInf : tl > kTau;
+        const bool need = tl > thr[i];
         if (__any(need)) {
           float tr = fmaxf(tl, shfl_xor(tl, 16));
           tr = fmaxf(tr, shfl_xor(tr, 32));
-          const float mn = fmaxf(m[i], mu + tr);
+          const float mn = fmaxf(m[i], mu[i] + tr);
           const float alpha = mn == kNegInf ? 1.0f : fast_exp2(m[i] - mn);
           l[i] *= alpha;
 #pragma unroll
@@ -294,10 +302,12 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) O[i][ct][e] *= ar;
           }
-          const float delta = mn == kNegInf ? 0.0f : mn - mu;
+          const float delta = mn == kNegInf ? 0.0f : mn - mu[i];
 #pragma unroll
           for (int e = 0; e < 8; ++e) xv[e] -= delta;
           m[i] = mn;
+          mu[i] = mn == kNegInf ? 0.0f : mn;
+          thr[i] = mn == kNegInf ? kNegInf : kTau;
         }
         float ps = 0.0f;
 #pragma unroll
@@ -308,9 +318,9 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
         }
         l[i] += ps;
       }
-      // P . V: V operands read once per column tile (transposed), shared by the query tiles
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
+      // P . V: V operands read once per column tile (transposed), shared by the
+      // query tiles, each read issued one column tile ahead of its use
+      auto vload = [&](int ct) __attribute__((always_inline)) {
         const int c = 2 * ct + ((col & 3) >> 1);
         const int r0 = 4 * quad + (col >> 2), r1 = r0 + 16;
         const uint16_t* p0 =
@@ -319,12 +329,19 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
             reinterpret_cast<const uint16_t*>(vt + (r1 * CPR + (c ^ (r1 % CPR))) * 16 + 8 * (col & 1));
         const s16x4 lo4 = lds_read_tr16(p0);
         const s16x4 hi4 = lds_read_tr16(p1);
-        const f16x8 bv = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        return __builtin_bit_cast(f16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      f16x8 bcur = vload(0);
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
-          if (i < MT - 1 || last_live) O[i][ct] = mfma_f16(A[i], bv, O[i][ct]);
+      for (int ct = 0; ct < NCT; ++ct) {
+        f16x8 bnext = bcur;
+        if (ct + 1 < NCT) bnext = vload(ct + 1);
+#pragma unroll
+        for (int i = 0; i < LIVE; ++i) O[i][ct] = mfma_f16(A[i], bcur, O[i][ct]);
+        bcur = bnext;
       }
-    }
+    };
+    if (wave_live) compute(std::integral_constant<int, MT>{});
     if (has_next) vwrite(t + 1, vnext);
     __syncthreads();
   }
