@@ -30,6 +30,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=25, help="untimed rounds; the clocks settle within ~50 ms of load")
     p.add_argument("--config", default="llama3_8b_layer_b8_l32k_int2_k32")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-full-kv-decode", action="store_true",
+                   help="skip the full-KV decode baseline (keeps per-kernel profiles to the path's own calls)")
     p.add_argument("--cpu-units", type=int, default=8, help="(b, kv-head) units in the CPU oracle sample")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain 1 GiB device-to-device copy, 3 times (the reference kernel for "
@@ -434,7 +436,8 @@ def main():
                    "ms_per_step": round(verify_total, 4)},
         "roofline": roof,
     }
-    line["full_kv_decode"] = full_kv_decode(w, dw, value, step_s)
+    if not a.no_full_kv_decode:
+        line["full_kv_decode"] = full_kv_decode(w, dw, value, step_s)
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, dw, int(n.sum()), a.cpu_units)
     print(json.dumps(line), flush=True)
