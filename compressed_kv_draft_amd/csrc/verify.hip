@@ -132,11 +132,9 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
     l[i] = 0.0f;
   }
   settle_compiler_loads();  // q is in registers before the key loop starts
-  const bool wave_live = tile0 + wave < tile_end;
-  // Only the last query tile needs a liveness guard: a wavefront with any live
-  // tile computes its earlier tiles unconditionally.  A dead one has zero
-  // queries and rlim = -1 and is never written out.
-  const bool last_live = tile0 + wave + kWaves * (MT - 1) < tile_end;
+  int n_live = 0;  // live query tiles of this wavefront (MT or MT - 1 by the plan)
+#pragma unroll
+  for (int i = 0; i < MT; ++i) n_live += tile0 + wave + kWaves * i < tile_end ? 1 : 0;
 
   // Staging: tile t's K and V go to ring slot t % kDepth by direct 16-byte
   // global->LDS loads issued kDepth - 1 tiles ahead; no registers hold them in flight.
@@ -226,6 +224,11 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
     vwrite(0, vr);
   }
   __syncthreads();
+  // The key loop, compiled for the number of live query tiles of this
+  // wavefront (MT or MT - 1; 0 only when MT is 1): a wavefront computes only
+  // its live tiles, and the choice is made once, outside the loop.
+  auto key_loop = [&](auto live_c) __attribute__((always_inline)) {
+  constexpr int LIVE = decltype(live_c)::value;
   for (int t = 0; t < ntiles; ++t) {
     const int t0 = kb + t * kKT;
     // ring slot (t + 3) % 4 was last read in step t - 1, which ended with a barrier
@@ -243,18 +246,17 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
     }
     const unsigned char* kt = smem + (t % kDepth) * TILE;
     const unsigned char* vt = smem + (kDepth + t % kDepth) * TILE;
-    // the tile's math for the first LIVE query tiles of this wavefront (LIVE is
-    // MT, or MT - 1 when the last one is dead): no per-tile guards inside, so
-    // each phase is one straight block the compiler can software-pipeline
-    auto compute = [&](auto live_c) __attribute__((always_inline)) {
-      constexpr int LIVE = decltype(live_c)::value;
+    // the tile's math for this wavefront's LIVE query tiles: no guards
+    // inside, so each phase is one straight block the compiler can
+    // software-pipeline
+    auto compute = [&]() __attribute__((always_inline)) {
       // scores for every query tile; K operands read once, shared by the tiles,
       // each read issued one step ahead of its use
       auto kread = [&](int idx) __attribute__((always_inline)) {
         const int row = 16 * (idx / NKS) + col, c = quad * (CPR / 4) + idx % NKS;
         return *reinterpret_cast<const bf16x8*>(kt + (row * CPR + (c ^ (row % CPR))) * 16);
       };
-      f32x4 s[LIVE][2];
+      f32x4 s[LIVE > 0 ? LIVE : 1][2];
 #pragma unroll
       for (int i = 0; i < LIVE; ++i) s[i][0] = s[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
       bf16x8 kcur = kread(0);
@@ -269,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
       }
       // mask only tiles that reach the drafted rows or the end of the range
       const bool need_mask = t0 + kKT > ctx || t0 + kKT > ke;
-      f16x8 A[LIVE];
+      f16x8 A[LIVE > 0 ? LIVE : 1];
 #pragma unroll
       for (int i = 0; i < LIVE; ++i) {
         float xv[8];
@@ -341,9 +343,15 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
         bcur = bnext;
       }
     };
-    if (wave_live) compute(std::integral_constant<int, MT>{});
+    if constexpr (LIVE > 0) compute();
     if (has_next) vwrite(t + 1, vnext);
     __syncthreads();
+  }
+  };
+  if (n_live == MT) {
+    key_loop(std::integral_constant<int, MT>{});
+  } else {
+    key_loop(std::integral_constant<int, MT - 1>{});
   }
 
   // finalise: the row sum over the 4 lanes of a column, then write o (or the
@@ -455,11 +463,10 @@ Plan plan_verify(int B, int Hq, int Hkv, int n_q, int max_ctx, int wpc) {
   const int g = Hq / Hkv;
   const int R = g * n_q;
   const int NT = (R + 15) / 16;
-  // full row groups of kWaves * kMaxMT tiles (every wavefront equally loaded)
-  // and one remainder group: a workgroup holds its slot for as long as its
-  // busiest wavefront runs, so this beats spreading the tiles evenly
-  const int per_group = NT < kWaves * kMaxMT ? NT : kWaves * kMaxMT;
-  p.rowgroups = (NT + per_group - 1) / per_group;
+  // as few row groups as hold the tiles at kMaxMT per wavefront, the tiles
+  // spread evenly over them (17 tiles: 9 + 8, not 12 + 5)
+  p.rowgroups = (NT + kWaves * kMaxMT - 1) / (kWaves * kMaxMT);
+  const int per_group = (NT + p.rowgroups - 1) / p.rowgroups;
   p.mt = (per_group + kWaves - 1) / kWaves;
   p.tiles_per_group = per_group;
   const int units = B * Hkv * p.rowgroups;
