@@ -259,15 +259,16 @@ __device__ __forceinline__ void rows_block(const RowSrc& src, int blk, const bf1
       myrow = (p >= 0 && p < src.bound) ? p : -1;
     }
   }
-  // K rows of tokens col and 16 + col, this quad's D/4 channels
+  // K rows of tokens col and 16 + col; k-step ks takes channels 32 ks + 8 quad
+  // .. + 7, so the four quads of a row read 64 contiguous bytes per load
   u32x4 kr[2][NKS];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
     const int pr = __shfl(myrow, 16 * tt + col, 64);
-    const uint16_t* p = src.k + (src.unit_row0 + (size_t)(pr < 0 ? 0 : pr)) * D + quad * (D / 4);
+    const uint16_t* p = src.k + (src.unit_row0 + (size_t)(pr < 0 ? 0 : pr)) * D + 8 * quad;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
-      kr[tt][ks] = pr >= 0 ? *reinterpret_cast<const u32x4*>(p + 8 * ks) : u32x4{0u, 0u, 0u, 0u};
+      kr[tt][ks] = pr >= 0 ? *reinterpret_cast<const u32x4*>(p + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
   }
   // V rows into LDS (row-major, padded pitch)
 #pragma unroll
@@ -343,14 +344,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
 
   uint16_t* vst = reinterpret_cast<uint16_t*>(smem + wave * C::ROWS_WAVE);  // exact-row path
 
-  // this lane's query head, channels quad * D/4 .. + D/4
-  const uint16_t* qrow = a.q + ((size_t)b * a.Hq + hk * g + head) * D + quad * (D / 4);
-  u32x4 qraw[NKS];
+  // this lane's query head: q for the exact rows' products (k-step ks takes
+  // channels 32 ks + 8 quad .. + 7), loaded where it is used
+  const uint16_t* qhead = a.q + ((size_t)b * a.Hq + hk * g + head) * D;
+  auto load_qb = [&](bf16x8 (&qb)[NKS]) __attribute__((always_inline)) {
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) qraw[ks] = *reinterpret_cast<const u32x4*>(qrow + 8 * ks);
-  bf16x8 qb[NKS];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, qraw[ks]);
+    for (int ks = 0; ks < NKS; ++ks) qb[ks] = *reinterpret_cast<const bf16x8*>(qhead + 8 * quad + 32 * ks);
+  };
 
   State<NCT, NV> st;
   st.m = kNegInf;
@@ -470,6 +470,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
     const int nb = (tl + 31) / 32;
     const int blo = (split - a.tail_first) * a.tail_bpw;
     const int bhi = min(blo + a.tail_bpw, nb);
+    bf16x8 qb[NKS];
+    load_qb(qb);
     for (int blk = blo + wave; blk < bhi; blk += kWaves)
       rows_block<D, NV>(src, blk, qb, a.scale_log2, vst, st, lane, col, quad, hilo);
     finish(a.main_splits + split - a.tail_first, false);
@@ -488,6 +490,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
       // q scaled per k slot (f16, exact): qF = q 2^(kQExp - bits*jj).  The zero-
       // point product needs q itself: for int4 that is qF (jj is 1), for int2
       // it comes from a workgroup table in LDS.
+      // q in the codes' channel order: k-step ks, channels quad * D/4 + 8 ks .. + 7
+      u32x4 qraw[NKS];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        qraw[ks] = *reinterpret_cast<const u32x4*>(qhead + quad * (D / 4) + 8 * ks);
       uint32_t qF[NKS][4];
       uint32_t* zero = reinterpret_cast<uint32_t*>(smem + C::ZERO_OFF);
       uint32_t* qzt = reinterpret_cast<uint32_t*>(smem + C::QZ_OFF);  // [head][quad][ks][4]
@@ -667,6 +674,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
       src.unit_row0 = unit_rows * a.L_cap;
       src.n_valid = a.n_main;
       src.bound = a.row_bound;
+      bf16x8 qb[NKS];
+      load_qb(qb);
       for (int blk = blo + wave; blk < bhi; blk += kWaves)
         rows_block<D, NV>(src, blk, qb, a.scale_log2, vst, st, lane, col, quad, hilo);
     }
