@@ -197,6 +197,77 @@ def test_verify_prefill_causal():
         assert_close(got[0, h * g:(h + 1) * g], ref, f"prefill h{h}")
 
 
+def test_verify_ragged_context_lengths():
+    """Each sequence of the batch has its own context length; the cache rows after
+    a sequence's ctx_len + n_q hold large values that must not leak into it."""
+    import torch
+    vc = _vc()
+    from compressed_kv_draft_amd.workload import bf16_dev
+    from synth.gen import f32_to_bf16_bits
+    print("[case] verify ragged ctx_len", flush=True)
+    rng = np.random.default_rng(11)
+    B, Hq, Hkv, D, n_q, L_cap = 3, 8, 2, 128, 9, 700
+    ctx = [600, 523, 17]
+    k = rng.standard_normal((B, Hkv, L_cap, D)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, L_cap, D)).astype(np.float32)
+    for b in range(B):
+        k[b, :, ctx[b] + n_q:] = 40.0      # would dominate every score if read
+        v[b, :, ctx[b] + n_q:] = 1000.0
+    q = rng.standard_normal((B, Hq, n_q, D)).astype(np.float32)
+    kb, vb, qb = (f32_to_bf16_bits(x) for x in (k, v, q))
+    full = vc.FullKV(bf16_dev(kb, "cuda"), bf16_dev(vb, "cuda"), L_cap=L_cap)
+    ctx_t = torch.tensor(ctx, dtype=torch.int32, device="cuda")
+    scale = O.scale_for(D)
+    got = vc.verify_attn(bf16_dev(qb, "cuda"), full, ctx_t, max(ctx), Hkv, scale).cpu().numpy()
+    g = Hq // Hkv
+    for b in range(B):
+        n = ctx[b] + n_q
+        for h in range(Hkv):
+            ref = O.verify_attention_unit(O.bf16_to_f64(qb[b, h * g:(h + 1) * g]), O.bf16_to_f64(kb[b, h, :n]),
+                                          O.bf16_to_f64(vb[b, h, :n]), ctx[b], scale)
+            assert_close(got[b, h * g:(h + 1) * g], ref, f"ragged ctx b{b} h{h}")
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_draft_ragged_tail_lengths(bits):
+    """Each sequence has its own exact-tail length (0 included): the rows past a
+    sequence's len hold large values that must not be read."""
+    import torch
+    vc = _vc()
+    from compressed_kv_draft_amd.workload import bf16_dev
+    from synth.gen import f32_to_bf16_bits
+    print(f"[case] draft ragged tail int{bits}", flush=True)
+    rng = np.random.default_rng(12 + bits)
+    B, Hq, Hkv, D, nq, T_cap = 3, 8, 2, 128, 256, 40
+    lens = [0, 5, 33]
+    k = rng.standard_normal((B, Hkv, nq, D)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, nq, D)).astype(np.float32)
+    tk = rng.standard_normal((B, Hkv, T_cap, D)).astype(np.float32)
+    tv = rng.standard_normal((B, Hkv, T_cap, D)).astype(np.float32)
+    for b in range(B):
+        tk[b, :, lens[b]:] = 40.0
+        tv[b, :, lens[b]:] = 1000.0
+    q = rng.standard_normal((B, Hq, D)).astype(np.float32)
+    kb, vb, tkb, tvb, qb = (f32_to_bf16_bits(x) for x in (k, v, tk, tv, q))
+    comp = vc.quantize_kv(bf16_dev(kb, "cuda"), bf16_dev(vb, "cuda"), bits, nq)
+    lens_t = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    tail = vc.Tail(bf16_dev(tkb, "cuda"), bf16_dev(tvb, "cuda"), lens_t)
+    scale = O.scale_for(D)
+    got = vc.draft_attn(comp, tail, bf16_dev(qb, "cuda"), scale).cpu().numpy()
+    g = Hq // Hkv
+    for b in range(B):
+        for h in range(Hkv):
+            kf = O.bf16_to_f64(kb[b, h]).astype(np.float32)
+            vf = O.bf16_to_f64(vb[b, h]).astype(np.float32)
+            kd = O.dequant_k(*O.quantize_k(kf, bits))
+            vd = O.dequant_v(*O.quantize_v(vf, bits))
+            keys, vals = O.draft_kv_rows("quant", k_deq=kd, v_deq=vd,
+                                         tail_k=O.bf16_to_f64(tkb[b, h, :lens[b]]),
+                                         tail_v=O.bf16_to_f64(tvb[b, h, :lens[b]]))
+            ref = O.draft_attention_unit(O.bf16_to_f64(qb[b, h * g:(h + 1) * g]), keys, vals, scale)
+            assert_close(got[b, h * g:(h + 1) * g], ref, f"ragged tail int{bits} b{b} h{h}")
+
+
 def test_verify_future_rows_do_not_leak():
     """Perturbing rows after L + j leaves verify position j bitwise unchanged."""
     from compressed_kv_draft_amd.workload import DeviceWorkload
