@@ -244,8 +244,10 @@ def cpu_baseline(w, dw, n_accept_sum, units):
 def e2e(a):
     """Tiny decoder end to end: prefill, then 256 greedy tokens by the loop.
     Every attention and token decision runs in libvc; the dense layers are
-    torch fp32.  Reports decode tokens/s (prefill excluded), the accepted-count
-    histogram, and whether the tokens equal the stored oracle sequence."""
+    torch fp32.  Drafting replays one recorded HIP graph per position (the
+    eager rate is reported beside it).  Reports decode tokens/s (prefill
+    excluded), the accepted-count histogram, and whether the tokens equal the
+    stored oracle sequence."""
     import numpy as np
     import torch
 
@@ -256,14 +258,18 @@ def e2e(a):
     W = M.weights(cfg)
     cos, sin = M.rope_tables(cfg)
     prompt = M.prompt(cfg)
-    runs = []
-    for i in range(a.warmup_e2e + a.steps_e2e):
-        lm = TinyLM(cfg, W, cos, sin)
-        toks, acc, st = lm.generate(prompt, cfg.n_gen)
-        if i >= a.warmup_e2e:
-            runs.append((toks, acc, st))
-        del lm
-        torch.cuda.empty_cache()
+    def timed(graph):
+        runs = []
+        for i in range(a.warmup_e2e + a.steps_e2e):
+            lm = TinyLM(cfg, W, cos, sin)
+            toks, acc, st = lm.generate(prompt, cfg.n_gen, graph=graph)
+            if i >= a.warmup_e2e:
+                runs.append((toks, acc, st))
+            del lm
+            torch.cuda.empty_cache()
+        return runs
+    eager = timed(False)
+    runs = timed(True)
     gold = None
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tests", "golden", f"e2e_{cfg.name}.txt")
     if os.path.exists(path):
@@ -283,6 +289,9 @@ def e2e(a):
             "rounds": st["rounds"], "accepted_per_round": acc, "accepted_histogram": hist,
             "mean_tokens_per_round": round(float(np.mean(np.array(acc) + 1)), 2),
             "decode_s": [round(x, 4) for x in dec], "prefill_s": round(st["prefill_s"], 4),
+            "drafting": "one HIP graph per draft position, replayed k times per round",
+            "eager_value": round((cfg.n_gen - 1) / min(r[2]["decode_s"] for r in eager), 1),
+            "graph_equals_eager": all(r[0] == toks and r[1] == acc for r in eager),
             "equals_oracle_greedy": (toks == gold) if gold is not None else None}
     print(json.dumps(line), flush=True)
 

@@ -153,11 +153,61 @@ class TinyLM:
     def _pos(self, pos: int) -> torch.Tensor:
         return torch.full((1,), pos, dtype=torch.int64, device=self.dev)
 
+    # ------------------------------------------------------------ graph-captured drafting
+
+    def _draft_step_dev(self):
+        """One draft position with all of its state on the device: token g_tok,
+        position g_pos, tail row g_row, draft slot g_j.  Writes the drafted
+        token into g_tok and g_drafts[g_j] and advances the counters, so the
+        same recorded work can be replayed for every position of a round."""
+        c = self.cfg
+        x = self.embed[self.g_tok.long()]
+        self.tail_len.copy_(self.g_row + 1)
+        for l in range(c.n_layers):
+            q, k, v = self._project(l, x, self.g_pos)
+            self.TK[l].index_copy_(2, self.g_row, k.unsqueeze(0))
+            self.TV[l].index_copy_(2, self.g_row, v.unsqueeze(0))
+            o = vc.draft_attn(self.comp[l], self.tails[l], q[:, :, 0].contiguous(), self.scale, out=self.q_out,
+                              ws=self.draft_ws, Hkv=c.Hkv)
+            x = self._finish(l, x, o[0][:, None, :])
+        vc.argmax(self._logits(x), ids=self.g_tok)
+        self.g_drafts.index_copy_(0, self.g_j, self.g_tok)
+        self.g_pos += 1
+        self.g_row += 1
+        self.g_j += 1
+
+    def _capture_draft_step(self):
+        """Record _draft_step_dev as a HIP graph (after one eager run, which sets
+        up library handles and the kernels' occupancy caches).  The recorded work
+        allocates nothing and sets no memory with hipMemset."""
+        dev = self.dev
+        self.g_tok = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.g_pos = torch.zeros(1, dtype=torch.int64, device=dev)
+        self.g_row = torch.zeros(1, dtype=torch.int64, device=dev)
+        self.g_j = torch.zeros(1, dtype=torch.int64, device=dev)
+        self.g_drafts = torch.zeros(self.cfg.k, dtype=torch.int32, device=dev)
+        saved = [(t.clone(), u.clone()) for t, u in zip(self.TK, self.TV)]
+        self.g_pos.fill_(self.cfg.prompt)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self._draft_step_dev()
+        torch.cuda.current_stream().wait_stream(s)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self._draft_step_dev()
+        for (t, u), T, V in zip(saved, self.TK, self.TV):   # undo the eager run's tail writes
+            T.copy_(t)
+            V.copy_(u)
+
     # ------------------------------------------------------------ the loop
 
-    def generate(self, prompt: np.ndarray, n_gen: int):
+    def generate(self, prompt: np.ndarray, n_gen: int, graph: bool = False):
         """Returns (tokens [n_gen] list, per-round accepted counts, stats dict
-        with timings and the logit of every emitted token)."""
+        with timings and the logit of every emitted token).  graph: replay a
+        HIP graph of one draft position k times per round instead of issuing
+        its ~200 launches from the host each time (recorded after the
+        prefill, outside the timed decode)."""
         c = self.cfg
         P = len(prompt)
         ids = torch.from_numpy(np.asarray(prompt, dtype=np.int32)).to(self.dev)
@@ -166,6 +216,10 @@ class TinyLM:
         lg = self.prefill(ids)
         pending = vc.argmax(lg[None])                       # int32 [1]
         torch.cuda.synchronize()
+        t_pre = time.perf_counter()
+        if graph:
+            self._capture_draft_step()
+            torch.cuda.synchronize()
         t1 = time.perf_counter()
         out = [int(pending.item())]
         top1 = [float(lg.max().item())]
@@ -173,10 +227,19 @@ class TinyLM:
         accepted = []
         drafts = torch.empty((1, c.k), dtype=torch.int32, device=self.dev)
         while len(out) < n_gen:
-            tok = pending
-            for j in range(c.k):
-                lgd = self.draft_step(tok, ctx + j, ctx - P + j)
-                tok = vc.argmax(lgd, ids=drafts[0, j:j + 1])
+            if graph:
+                self.g_tok.copy_(pending)
+                self.g_pos.fill_(ctx)
+                self.g_row.fill_(ctx - P)
+                self.g_j.zero_()
+                for j in range(c.k):
+                    self.graph.replay()
+                drafts[0].copy_(self.g_drafts)
+            else:
+                tok = pending
+                for j in range(c.k):
+                    lgd = self.draft_step(tok, ctx + j, ctx - P + j)
+                    tok = vc.argmax(lgd, ids=drafts[0, j:j + 1])
             seq = torch.cat([pending, drafts[0]])
             x = self.causal_pass(seq, ctx)
             vlog = self._logits(x)
@@ -195,6 +258,6 @@ class TinyLM:
         torch.cuda.synchronize()
         t2 = time.perf_counter()
         out = out[:n_gen]
-        stats = dict(prefill_s=t1 - t0, decode_s=t2 - t1, rounds=len(accepted), top1=top1[:n_gen],
+        stats = dict(prefill_s=t_pre - t0, decode_s=t2 - t1, rounds=len(accepted), top1=top1[:n_gen], graph=graph,
                      tokens_per_s=(len(out) - 1) / (t2 - t1) if t2 > t1 else 0.0)
         return out, accepted, stats

@@ -36,12 +36,12 @@ def _golden(cfg):
     return kv
 
 
-def _run(cfg):
+def _run(cfg, graph=False, W=None):
     from compressed_kv_draft_amd.tinylm import TinyLM
-    W = M.weights(cfg)
+    W = M.weights(cfg) if W is None else W
     cos, sin = M.rope_tables(cfg)
     lm = TinyLM(cfg, W, cos, sin)
-    return lm.generate(M.prompt(cfg), cfg.n_gen)
+    return lm.generate(M.prompt(cfg), cfg.n_gen, graph=graph)
 
 
 def _compare(cfg, toks, acc, stats, want, want_top1, margins):
@@ -62,15 +62,23 @@ def _compare(cfg, toks, acc, stats, want, want_top1, margins):
 
 
 def test_e2e_tiny_lm_equals_oracle_greedy():
+    """Both ways of drafting (eager launches, and one recorded HIP graph per
+    draft position replayed k times a round) reproduce the oracle's tokens and
+    take identical drafts (equal accepted counts)."""
     cfg = C.LM_E2E
     g = _golden(cfg)
     assert g["config"] == cfg.name
     assert float(g["q_gain"]) == cfg.q_gain and float(g["plant"]) == cfg.plant and int(g["seed"]) == cfg.seed
-    print(f"[case] e2e {cfg.name}", flush=True)
-    toks, acc, stats = _run(cfg)
     want = [int(x) for x in g["tokens"].split()]
-    _compare(cfg, toks, acc, stats, want, [float(x) for x in g["top1"].split()],
-             [float(x) for x in g["margin"].split()])
+    W = M.weights(cfg)
+    runs = {}
+    for graph in (False, True):
+        print(f"[case] e2e {cfg.name} graph={graph}", flush=True)
+        toks, acc, stats = _run(cfg, graph=graph, W=W)
+        _compare(cfg, toks, acc, stats, want, [float(x) for x in g["top1"].split()],
+                 [float(x) for x in g["margin"].split()])
+        runs[graph] = (toks, acc)
+    assert runs[True] == runs[False]
 
 
 def test_e2e_small_lm_equals_oracle_greedy():
@@ -80,5 +88,10 @@ def test_e2e_small_lm_equals_oracle_greedy():
     cos, sin = M.rope_tables(cfg)
     m = E.Model(cfg, M.weights(cfg), cos, sin)
     want, top, marg = E.greedy_decode(m, M.prompt(cfg), cfg.n_gen)
-    toks, acc, stats = _run(cfg)
-    _compare(cfg, toks, acc, stats, [int(x) for x in want], list(top), list(marg))
+    runs = {}
+    for graph in (False, True):
+        print(f"[case] e2e {cfg.name} graph={graph}", flush=True)
+        toks, acc, stats = _run(cfg, graph=graph)
+        _compare(cfg, toks, acc, stats, [int(x) for x in want], list(top), list(marg))
+        runs[graph] = (toks, acc)
+    assert runs[True] == runs[False]
