@@ -6,9 +6,9 @@
 //
 // The g query heads of a GQA group times the n_q positions form R = g * n_q
 // query rows that share one KV head, so q.K^T and P.V are real contractions.
-// Per 32-key tile a workgroup (4 wavefronts) stages K (bf16, padded rows) and
-// V (converted to f16) in LDS once; every wavefront owns up to MT 16-row query
-// tiles and computes, for each,
+// Per 32-key tile a workgroup (4 or 8 wavefronts) stages K (bf16, padded rows)
+// and V (converted to f16) in LDS once; every wavefront owns up to MT 16-row
+// query tiles and computes, for each,
 //   S[32 keys x 16 rows] = K . Q^T   (bf16 MFMA: keys are the A rows, so each
 //                                     lane ends up with 8 keys of one row)
 //   online softmax per row in fp32 (lazy rescale, running max moves by >= 2^8)
@@ -17,8 +17,10 @@
 // The K and V operands of a tile are read from LDS once per wavefront and
 // shared by its query tiles.  LDS is double-buffered with one barrier per tile;
 // the next tile's global loads are in flight during the current tile's math.
-// Query rows beyond 3 tiles per wavefront go to further row groups, laid out so
-// that the row groups of one key range run on the same XCD (shared L2).
+// A workgroup has 8 wavefronts when 4 cannot hold every query tile (a GQA group
+// of 8 at k = 32 has 17), so that the cache is read from HBM once.  Query rows
+// beyond 3 tiles per wavefront go to further row groups, laid out so that the
+// row groups of one key range run on the same XCD.
 #include <map>
 #include <mutex>
 #include <type_traits>
@@ -30,8 +32,7 @@
 namespace vc {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kWaves = 4;     // wavefronts per workgroup, or 2 * kWaves for many query tiles
 constexpr int kKT = 32;       // keys per tile
 constexpr int kMaxMT = 3;     // query tiles per wavefront
 constexpr int kDepth = 4;     // K/V tiles in the LDS ring
@@ -51,7 +52,7 @@ struct VerifyArgs {
   float* out;
   float* ws;
   int B, Hq, Hkv, g, n_q, R, NT;
-  int rowgroups, tiles_per_group;  // query tiles per workgroup = kWaves * MT
+  int rowgroups, tiles_per_group;  // query tiles per workgroup <= NW * MT
   int splits, keys_per_split;
   int n_su;                        // splits * units
   float scale_log2;
@@ -68,14 +69,16 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 w) {
   return r;
 }
 
-template <int D, int MT, bool PAGED>
-__global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
+template <int D, int MT, bool PAGED, int NW>
+__global__ __launch_bounds__(64 * NW) void verify_mfma_kernel(VerifyArgs a) {
   constexpr int NKS = D / 32, NCT = D / 16;
   constexpr int CPR = D / 8;                      // 16-byte chunks per key row
   constexpr int TILE = kKT * D * 2;               // bytes of one K or V tile
-  constexpr int ROUNDS = TILE / (16 * kThreads);  // direct loads per thread per tile and tensor
-  static_assert(TILE % (16 * kThreads) == 0, "a tile is whole rounds of 16-byte loads");
-  constexpr int NDMA = 2 * ROUNDS;                // load instructions per thread per tile
+  // wavefronts that stage tiles (one 1 KiB load instruction each per round)
+  constexpr int LW = TILE / 1024 < NW ? TILE / 1024 : NW;
+  constexpr int ROUNDS = TILE / (1024 * LW);      // direct loads per staging thread per tile and tensor
+  static_assert(TILE % (1024 * LW) == 0, "a tile is whole rounds of 16-byte loads");
+  constexpr int NDMA = 2 * ROUNDS;                // load instructions per staging thread per tile
   // ring of kDepth K tiles, then kDepth V tiles (bf16 as loaded, f16 once converted)
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kDepth * TILE];
 
@@ -99,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
   const int kb = split * a.keys_per_split;
   const int ke = min(kb + a.keys_per_split, key_end);
 
-  // this wavefront's query tiles: tile0 + wave + kWaves * i
+  // this wavefront's query tiles: tile0 + wave + NW * i
   const int tile0 = rg * a.tiles_per_group;
   const int tile_end = min(tile0 + a.tiles_per_group, a.NT);
   bf16x8 qb[MT][NKS];
@@ -111,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
   int rlim[MT];
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
-    const int tile = tile0 + wave + kWaves * i;
+    const int tile = tile0 + wave + NW * i;
     const int r = tile * 16 + col;
     rlim[i] = -1;
     if (tile < tile_end && r < a.R) {
@@ -134,11 +137,12 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
   settle_compiler_loads();  // q is in registers before the key loop starts
   int n_live = 0;  // live query tiles of this wavefront (MT or MT - 1 by the plan)
 #pragma unroll
-  for (int i = 0; i < MT; ++i) n_live += tile0 + wave + kWaves * i < tile_end ? 1 : 0;
+  for (int i = 0; i < MT; ++i) n_live += tile0 + wave + NW * i < tile_end ? 1 : 0;
 
   // Staging: tile t's K and V go to ring slot t % kDepth by direct 16-byte
   // global->LDS loads issued kDepth - 1 tiles ahead; no registers hold them in flight.
-  // In round r this thread fills LDS chunk s = (r * kWaves + wave) * 64 + lane
+  // In round r a thread of staging wavefront wave < LW fills LDS chunk
+  // s = (r * LW + wave) * 64 + lane
   // of the tile, which holds 16-byte chunk (s % CPR) ^ (key % CPR) of key row
   // key = s / CPR: the XOR swizzle makes the operand reads below conflict-free.
   // The rows of one load instruction lie in one page (pages hold >= 8 rows).
@@ -152,18 +156,19 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
   const cptr ptab = (cptr)(a.page_table);
   uint32_t zfill = 0;  // bit (slot * ROUNDS + r): that round of that ring slot reads as zeros
   auto issue = [&](int t) __attribute__((always_inline)) {
+    if (LW < NW && wave >= LW) return;
     const int t0 = kb + t * kKT;
     const int sl = t % kDepth;
     const uint32_t kl = lds0 + sl * TILE, vl = lds0 + (kDepth + sl) * TILE;
 #pragma unroll
     for (int r = 0; r < ROUNDS; ++r) {
-      const int s = (r * kWaves + wave) * 64 + lane;
+      const int s = (r * LW + wave) * 64 + lane;
       const int row = s / CPR, cc = (s % CPR) ^ (row % CPR);
       // rows past the split's range are clamped to its last row (masked later)
       const int key = min(t0 + row, ke - 1);
       const unsigned char *kp, *vp;
       if constexpr (PAGED) {
-        const int key0 = min(t0 + (r * kWaves + wave) * (64 / CPR), ke - 1);  // wave-uniform
+        const int key0 = min(t0 + (r * LW + wave) * (64 / CPR), ke - 1);  // wave-uniform
         int pslot = ptab[(size_t)b * a.pages_per_seq + (key0 >> a.page_log2)];
         const bool bad = pslot < 0 || pslot >= a.n_slots;
         const uint32_t bit = 1u << (sl * ROUNDS + r);
@@ -176,8 +181,8 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
         kp = kv8 + ((unit_row0 + key) * D) * 2 + cc * 16;
         vp = vv8 + ((unit_row0 + key) * D) * 2 + cc * 16;
       }
-      lds_dma16(kp, kl + (r * kWaves + wave) * 1024);
-      lds_dma16(vp, vl + (r * kWaves + wave) * 1024);
+      lds_dma16(kp, kl + (r * LW + wave) * 1024);
+      lds_dma16(vp, vl + (r * LW + wave) * 1024);
     }
   };
   // once tile u has landed: each lane converts the V chunks it loaded to f16 in
@@ -185,16 +190,18 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
   // issued before the current tile's math, and a write after it, so the LDS
   // read latency hides behind the math.
   auto vread = [&](int u, u32x4 (&vr)[ROUNDS]) __attribute__((always_inline)) {
+    if (LW < NW && wave >= LW) return;
     const int sl = u % kDepth;
 #pragma unroll
     for (int r = 0; r < ROUNDS; ++r)
-      vr[r] = *reinterpret_cast<const u32x4*>(smem + (kDepth + sl) * TILE + ((r * kWaves + wave) * 64 + lane) * 16);
+      vr[r] = *reinterpret_cast<const u32x4*>(smem + (kDepth + sl) * TILE + ((r * LW + wave) * 64 + lane) * 16);
   };
   auto vwrite = [&](int u, const u32x4 (&vr)[ROUNDS]) __attribute__((always_inline)) {
+    if (LW < NW && wave >= LW) return;
     const int sl = u % kDepth;
 #pragma unroll
     for (int r = 0; r < ROUNDS; ++r) {
-      const int s = (r * kWaves + wave) * 64 + lane;
+      const int s = (r * LW + wave) * 64 + lane;
       u32x4* vc = reinterpret_cast<u32x4*>(smem + (kDepth + sl) * TILE + s * 16);
       if (PAGED && (zfill >> (sl * ROUNDS + r)) & 1u) {
         *vc = u32x4{0u, 0u, 0u, 0u};
@@ -359,7 +366,7 @@ __global__ __launch_bounds__(kThreads) void verify_mfma_kernel(VerifyArgs a) {
   // whose max and sum live in the lanes with col == 4q+e.
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
-    const int tile = tile0 + wave + kWaves * i;
+    const int tile = tile0 + wave + NW * i;
     if (tile >= tile_end) continue;  // wave-uniform
     float lt = l[i];
     lt += shfl_xor(lt, 16);
@@ -431,14 +438,19 @@ __global__ __launch_bounds__(128) void verify_combine_kernel(const float* __rest
 
 typedef void (*VerifyKernel)(VerifyArgs);
 
-template <int D, bool PAGED>
-VerifyKernel pick(int mt) {
-  if (mt == 1) return verify_mfma_kernel<D, 1, PAGED>;
-  if (mt == 2) return verify_mfma_kernel<D, 2, PAGED>;
-  return verify_mfma_kernel<D, 3, PAGED>;
+template <int D, bool PAGED, int NW>
+VerifyKernel pick_mt(int mt) {
+  if (mt == 1) return verify_mfma_kernel<D, 1, PAGED, NW>;
+  if (mt == 2) return verify_mfma_kernel<D, 2, PAGED, NW>;
+  return verify_mfma_kernel<D, 3, PAGED, NW>;
 }
 
-int wgs_per_cu(VerifyKernel k) {
+template <int D, bool PAGED>
+VerifyKernel pick(int mt, int nw) {
+  return nw == 8 ? pick_mt<D, PAGED, 8>(mt) : pick_mt<D, PAGED, 4>(mt);
+}
+
+int wgs_per_cu(VerifyKernel k, int threads) {
   static std::mutex mu;
   static std::map<std::pair<const void*, int>, int> cache;
   int dev = 0;
@@ -448,13 +460,13 @@ int wgs_per_cu(VerifyKernel k) {
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kThreads, 0) != hipSuccess || n < 1) n = 2;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, threads, 0) != hipSuccess || n < 1) n = 1;
   cache[key] = n;
   return n;
 }
 
 struct Plan {
-  int mt, tiles_per_group, rowgroups, splits, kps;
+  int nw, mt, tiles_per_group, rowgroups, splits, kps;
 };
 
 // wpc: resident workgroups per CU of the kernel (8 bounds every variant).
@@ -463,11 +475,12 @@ Plan plan_verify(int B, int Hq, int Hkv, int n_q, int max_ctx, int wpc) {
   const int g = Hq / Hkv;
   const int R = g * n_q;
   const int NT = (R + 15) / 16;
-  // as few row groups as hold the tiles at kMaxMT per wavefront, the tiles
-  // spread evenly over them (17 tiles: 9 + 8, not 12 + 5)
-  p.rowgroups = (NT + kWaves * kMaxMT - 1) / (kWaves * kMaxMT);
+  // 8 wavefronts when 4 cannot hold every tile at kMaxMT each; then as few row
+  // groups as hold the tiles, the tiles spread evenly over them
+  p.nw = NT > kWaves * kMaxMT ? 2 * kWaves : kWaves;
+  p.rowgroups = (NT + p.nw * kMaxMT - 1) / (p.nw * kMaxMT);
   const int per_group = (NT + p.rowgroups - 1) / p.rowgroups;
-  p.mt = (per_group + kWaves - 1) / kWaves;
+  p.mt = (per_group + p.nw - 1) / p.nw;
   p.tiles_per_group = per_group;
   const int units = B * Hkv * p.rowgroups;
   const int keys = max_ctx + n_q;
@@ -544,9 +557,9 @@ extern "C" int vc_verify_attn(const void* q, const vc_kv_full* kv, const int32_t
   a.scale_log2 = scale * kLog2e;
   Plan p = plan_verify(B, Hq, Hkv, n_q, max_ctx, 8);
   const bool paged = kv->page_table != nullptr;
-  const VerifyKernel kern = D == 128 ? (paged ? pick<128, true>(p.mt) : pick<128, false>(p.mt))
-                                     : (paged ? pick<64, true>(p.mt) : pick<64, false>(p.mt));
-  p = plan_verify(B, Hq, Hkv, n_q, max_ctx, wgs_per_cu(kern));
+  const VerifyKernel kern = D == 128 ? (paged ? pick<128, true>(p.mt, p.nw) : pick<128, false>(p.mt, p.nw))
+                                     : (paged ? pick<64, true>(p.mt, p.nw) : pick<64, false>(p.mt, p.nw));
+  p = plan_verify(B, Hq, Hkv, n_q, max_ctx, wgs_per_cu(kern, 64 * p.nw));
   a.rowgroups = p.rowgroups;
   a.tiles_per_group = p.tiles_per_group;
   a.splits = p.splits;
@@ -562,7 +575,7 @@ extern "C" int vc_verify_attn(const void* q, const vc_kv_full* kv, const int32_t
   }
   // 1-D grid: 8 consecutive (split, unit) pairs per group of 8 * rowgroups workgroups
   const int n_wg = ((a.n_su + 7) / 8) * 8 * p.rowgroups;
-  kern<<<n_wg, kThreads, 0, stream>>>(a);
+  kern<<<n_wg, 64 * p.nw, 0, stream>>>(a);
   VC_HIP(hipGetLastError());
   if (p.splits > 1) {
     const int rows = B * Hq * n_q;
