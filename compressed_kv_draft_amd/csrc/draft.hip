@@ -104,7 +104,7 @@ struct Cfg {
                               lds_dma_count(VM_BYTES);  // load instructions per block
   // shared by the workgroup's wavefronts: zeros, and (int2) the query as f16
   static constexpr int ZERO_BYTES = 64 * NKS;
-  static constexpr int QZ_BYTES = BITS == 2 ? 8 * 4 * NKS * 16 : 0;  // [head][quad][ks] u32x4
+  static constexpr int QZ_BYTES = BITS == 2 ? 8 * 4 * NKS * 16 : 0;  // [ks][quad][head] u32x4
   static constexpr int SHARED_BYTES = BITS == 0 ? 0 : ZERO_BYTES + QZ_BYTES;
   // ring slots per wavefront: up to 4; as many as leave room for 4 workgroups
   // per CU if that gives at least 2, else for 3
@@ -182,28 +182,39 @@ __device__ __forceinline__ float f16lo(uint32_t w) { return (float)__builtin_bit
 __device__ __forceinline__ float f16hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[1]; }
 
 // Per-lane softmax state: running max m (log2 units) of this lane's head, the
-// partial sum l over this lane's tokens, zero-point sums, output accumulators.
+// offset mu the scores are taken relative to (m, or 0 while m is -inf), the
+// amount thr a block max must exceed to move m (-inf while m is -inf, else
+// kTau), the partial sum l over this lane's tokens, zero-point sums, output
+// accumulators.
 template <int NCT, int NV>
 struct State {
-  float m, l;
+  float m, mu, thr, l;
   float zacc[NV];
   f32x4 O[NCT];
+  __device__ __forceinline__ void clear() {
+    m = kNegInf;
+    mu = 0.0f;
+    thr = kNegInf;
+    l = 0.0f;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) zacc[v] = 0.0f;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) O[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 };
 
 // Online softmax over the 8 scores a lane holds for one block (its head, tokens
-// 4q..4q+3 and 16+4q..16+4q+3).  Scores arrive relative to mu = m (0 while m is
-// still -inf).  The running max only moves when some score exceeds it by kTau, so
+// 4q..4q+3 and 16+4q..16+4q+3).  Scores arrive relative to st.mu.  The running max only moves when some score exceeds it by kTau, so
 // in the common case no cross-lane reduction and no rescale happen; P <= 2^kTau.
 template <int NCT, int NV>
 __device__ __forceinline__ void softmax_block(float (&x)[8], State<NCT, NV>& st, float (&P)[8], int quad) {
   float tl = x[0];
 #pragma unroll
   for (int e = 1; e < 8; ++e) tl = fmaxf(tl, x[e]);
-  const bool need = st.m == kNegInf ? tl > kNegInf : tl > kTau;
-  if (__any(need)) {
+  if (__any(tl > st.thr)) {
     float tr = fmaxf(tl, shfl_xor(tl, 16));
     tr = fmaxf(tr, shfl_xor(tr, 32));  // max over the head's tokens of this block
-    const float mu = st.m == kNegInf ? 0.0f : st.m;
+    const float mu = st.mu;
     const float mn = fmaxf(st.m, mu + tr);
     const float alpha = mn == kNegInf ? 1.0f : fast_exp2(st.m - mn);
     st.l *= alpha;
@@ -220,6 +231,8 @@ __device__ __forceinline__ void softmax_block(float (&x)[8], State<NCT, NV>& st,
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] -= delta;
     st.m = mn;
+    st.mu = mn == kNegInf ? 0.0f : mn;
+    st.thr = mn == kNegInf ? kNegInf : kTau;
   }
   float ps = 0.0f;
 #pragma unroll
@@ -229,8 +242,6 @@ __device__ __forceinline__ void softmax_block(float (&x)[8], State<NCT, NV>& st,
   }
   st.l += ps;
 }
-
-__device__ __forceinline__ float mu_of(float m) { return m == kNegInf ? 0.0f : m; }
 
 // Source of exact bf16 rows: the tail, the identity cache or the kept rows.
 struct RowSrc {
@@ -281,7 +292,7 @@ __device__ __forceinline__ void rows_block(const RowSrc& src, int blk, const bf1
     *reinterpret_cast<u32x4*>(vst + row * VPITCH + off) = val;
   }
   // scores (log2 units, relative to the running max), invalid rows masked
-  const float mu = mu_of(st.m);
+  const float mu = st.mu;
   float x[8];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
@@ -353,12 +364,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
   };
 
   State<NCT, NV> st;
-  st.m = kNegInf;
-  st.l = 0.0f;
-#pragma unroll
-  for (int v = 0; v < NV; ++v) st.zacc[v] = 0.0f;
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) st.O[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.clear();
 
   const size_t unit_rows = (size_t)unit;
 
@@ -445,14 +451,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
       }
     }
   };
-  auto reset = [&]() __attribute__((always_inline)) {
-    st.m = kNegInf;
-    st.l = 0.0f;
-#pragma unroll
-    for (int v = 0; v < NV; ++v) st.zacc[v] = 0.0f;
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) st.O[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  };
 
   // ---------------------------------------------------------- exact tail
   // (the last workgroups first take a range of the exact rows, as a partial
@@ -475,7 +473,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
     for (int blk = blo + wave; blk < bhi; blk += kWaves)
       rows_block<D, NV>(src, blk, qb, a.scale_log2, vst, st, lane, col, quad, hilo);
     finish(a.main_splits + split - a.tail_first, false);
-    reset();
+    st.clear();
     __syncthreads();  // the epilogue's LDS is reused below
   }
 
@@ -497,7 +495,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
         qraw[ks] = *reinterpret_cast<const u32x4*>(qhead + quad * (D / 4) + 8 * ks);
       uint32_t qF[NKS][4];
       uint32_t* zero = reinterpret_cast<uint32_t*>(smem + C::ZERO_OFF);
-      uint32_t* qzt = reinterpret_cast<uint32_t*>(smem + C::QZ_OFF);  // [head][quad][ks][4]
+      uint32_t* qzt = reinterpret_cast<uint32_t*>(smem + C::QZ_OFF);  // [ks][quad][head][4]: a quad's heads in consecutive 16-byte chunks
       {
         const uint16_t* qh = reinterpret_cast<const uint16_t*>(qraw);
 #pragma unroll
@@ -515,7 +513,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
             z4[i] = __builtin_bit_cast(uint32_t, pz);
           }
           if (BITS == 2 && wave == 0 && rep == 0 && hilo == 0)
-            *reinterpret_cast<u32x4*>(qzt + ((head * 4 + quad) * NKS + ks) * 4) = z4;
+            *reinterpret_cast<u32x4*>(qzt + ((ks * 4 + quad) * 8 + head) * 4) = z4;
         }
       }
       for (int i = threadIdx.x; i < C::ZERO_BYTES / 4; i += kThreads) zero[i] = 0u;
@@ -580,7 +578,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
           if constexpr (BITS == 4) {
             qz4 = u32x4{qF[ks][0], qF[ks][1], qF[ks][2], qF[ks][3]};
           } else {
-            qz4 = *reinterpret_cast<const u32x4*>(qzt + ((head * 4 + quad) * NKS + ks) * 4);
+            qz4 = *reinterpret_cast<const u32x4*>(qzt + ((ks * 4 + quad) * 8 + head) * 4);
           }
           accZ = mfma_f16(__builtin_bit_cast(f16x8, z4), __builtin_bit_cast(f16x8, qz4), accZ);
           const u32x4 s4 = *reinterpret_cast<const u32x4*>(sp + o);
@@ -599,7 +597,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
         }
         // code part of q.k for tokens col and 16 + col; hi + lo columns summed
         const float code_scale = 0x1p20f * a.scale_log2;  // undoes 2^-24 (codes) * 2^kQExp (q)
-        const float zpart = fmaf(accZ[0], a.scale_log2, -mu_of(st.m));  // rows of accZ all hold z . q
+        const float zpart = fmaf(accZ[0], a.scale_log2, -st.mu);  // rows of accZ all hold z . q
         float x[8];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -635,18 +633,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
           const u32x4 m0 = *reinterpret_cast<const u32x4*>(vmg);
           const u32x4 m1 = *reinterpret_cast<const u32x4*>(vmg + 4);
           const uint32_t mm[8] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
+          // hi = RN_f16 of the fp32 product P s (two per packed conversion); lo =
+          // RN_f16 of the residual P s - hi, taken in one fma against the rounded
+          // hi, so that hi + lo carries P s to about 22 significant bits.
           float zs = 0.0f;
-          _Float16 hv[8], lv[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const f16x2 sz = __builtin_bit_cast(f16x2, mm[e]);
-            const float sc = (float)sz[0];
-            hv[e] = (_Float16)fmaf(P[e], sc, 0.0f);
-            lv[e] = (_Float16)fmaf(P[e], sc, -(float)hv[e]);
-            zs = fmaf(P[e], (float)sz[1], zs);
+          for (int e = 0; e < 8; e += 2) {
+            const f16x2 s0 = __builtin_bit_cast(f16x2, mm[e]), s1 = __builtin_bit_cast(f16x2, mm[e + 1]);
+            const f32x2 h32 = {fmaf(P[e], (float)s0[0], -0.0f), fmaf(P[e + 1], (float)s1[0], -0.0f)};
+            const f16x2 h = __builtin_convertvector(h32, f16x2);
+            const f32x2 l32 = {fmaf(P[e], (float)s0[0], -(float)h[0]), fmaf(P[e + 1], (float)s1[0], -(float)h[1])};
+            const f16x2 lo = __builtin_convertvector(l32, f16x2);
+            Ahi[v][e] = h[0];
+            Ahi[v][e + 1] = h[1];
+            Alo[v][e] = lo[0];
+            Alo[v][e + 1] = lo[1];
+            zs = fmaf(P[e], (float)s0[1], zs);
+            zs = fmaf(P[e + 1], (float)s1[1], zs);
           }
-          Ahi[v] = f16x8{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]};
-          Alo[v] = f16x8{lv[0], lv[1], lv[2], lv[3], lv[4], lv[5], lv[6], lv[7]};
           st.zacc[v] += zs;
         }
         // P.V code part
