@@ -5,6 +5,7 @@ loudly if it is missing: every step of the path runs in its HIP kernels.
 """
 from ._lib import (  # noqa: F401
     LIB, VcError, Compressed, Tail, FullKV, version, quantize_kv, identity_cache, token_drop_cache,
-    debug_dequant, draft_ws_bytes, draft_attn, verify_ws_bytes, verify_attn, argmax, accept,
+    debug_dequant, draft_ws_bytes, draft_attn, verify_ws_bytes, verify_attn, verify_range_parts,
+    verify_attn_range, verify_merge, argmax, accept,
     prefetch_full_kv,
 )

@@ -50,6 +50,10 @@ EXPORTS = {
     "vc_verify_ws_bytes": (c_size, [c_int, c_int, c_int, c_int, c_int, c_int]),
     "vc_verify_attn": (c_int, [c_void, ctypes.POINTER(VcKvFull), c_void, c_int, c_int, c_void,
                                c_int, c_int, c_int, c_int, c_float, c_void, c_size, c_void]),
+    "vc_verify_range_parts": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int]),
+    "vc_verify_attn_range": (c_int, [c_void, ctypes.POINTER(VcKvFull), c_void, c_int, c_int, c_int, c_int, c_void,
+                                     c_int, c_int, c_int, c_int, c_float, c_void]),
+    "vc_verify_merge": (c_int, [c_void, c_int, c_int, c_int, c_int, c_int, c_void, c_void]),
     "vc_argmax": (c_int, [c_void, c_int, c_int, c_void, c_void]),
     "vc_accept": (c_int, [c_void, c_void, c_int, c_int, c_int, c_void, c_void, c_void]),
     "vc_prefetch_full_kv": (c_int, [c_void, c_size, c_int, c_void, c_int, c_int, c_void, c_int,
@@ -216,6 +220,37 @@ def verify_attn(q: torch.Tensor, kv: FullKV, ctx_len: torch.Tensor, max_ctx: int
     rc = LIB.vc_verify_attn(_ptr(q), ctypes.byref(kv.desc), _ptr(ctx_len), int(max_ctx), n_q, _ptr(out),
                             B, Hq, Hkv, D, float(scale), _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, "vc_verify_attn")
+    return out
+
+
+def verify_range_parts(B, Hq, Hkv, D, n_q, key_begin, key_end) -> int:
+    """Partial slots one vc_verify_attn_range call over [key_begin, key_end) writes."""
+    return int(LIB.vc_verify_range_parts(B, Hq, Hkv, D, n_q, key_begin, key_end))
+
+
+def verify_attn_range(q: torch.Tensor, kv: FullKV, ctx_len: torch.Tensor, max_ctx: int, Hkv: int, scale: float,
+                      key_begin: int, key_end: int, parts: torch.Tensor, stream=None) -> int:
+    """Verify partials over keys [key_begin, key_end) into `parts` (fp32, at least
+    verify_range_parts(...) * B*Hq*n_q*(D+2) elements, slots back to back).
+    Returns the number of slots written."""
+    B, Hq, n_q, D = q.shape
+    n = verify_range_parts(B, Hq, Hkv, D, n_q, key_begin, key_end)
+    if n <= 0 or parts.numel() < n * B * Hq * n_q * (D + 2) or parts.dtype != torch.float32:
+        raise VcError(f"vc_verify_attn_range: parts too small or not fp32 ({parts.numel()} < {n} slots)")
+    rc = LIB.vc_verify_attn_range(_ptr(q), ctypes.byref(kv.desc), _ptr(ctx_len), int(max_ctx), n_q, int(key_begin),
+                                  int(key_end), _ptr(parts), B, Hq, Hkv, D, float(scale), _stream(stream))
+    _check(rc, "vc_verify_attn_range")
+    return n
+
+
+def verify_merge(parts: torch.Tensor, n_parts: int, B: int, Hq: int, n_q: int, D: int, out=None, stream=None):
+    """Merge n_parts consecutive verify partial slots into fp32 [B, Hq, n_q, D]."""
+    if out is None:
+        out = torch.empty((B, Hq, n_q, D), dtype=torch.float32, device=parts.device)
+    if parts.numel() < n_parts * B * Hq * n_q * (D + 2):
+        raise VcError("vc_verify_merge: parts holds fewer slots than n_parts")
+    rc = LIB.vc_verify_merge(_ptr(parts), int(n_parts), B, Hq, n_q, D, _ptr(out), _stream(stream))
+    _check(rc, "vc_verify_merge")
     return out
 
 

@@ -54,6 +54,8 @@ struct VerifyArgs {
   int B, Hq, Hkv, g, n_q, R, NT;
   int rowgroups, tiles_per_group;  // query tiles per workgroup <= NW * MT
   int splits, keys_per_split;
+  int key_begin, key_limit;        // keys [key_begin, key_limit) of every sequence, clipped to ctx_len + n_q
+  int write_partials;              // 1: always write split partials to ws (range calls), never the output
   int n_su;                        // splits * units
   float scale_log2;
 };
@@ -98,8 +100,8 @@ __global__ __launch_bounds__(64 * NW) void verify_mfma_kernel(VerifyArgs a) {
 
   int ctx = a.ctx_len[b];
   ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
-  const int key_end = ctx + a.n_q;
-  const int kb = split * a.keys_per_split;
+  const int key_end = min(ctx + a.n_q, a.key_limit);
+  const int kb = a.key_begin + split * a.keys_per_split;
   const int ke = min(kb + a.keys_per_split, key_end);
 
   // this wavefront's query tiles: tile0 + wave + NW * i
@@ -380,7 +382,7 @@ __global__ __launch_bounds__(64 * NW) void verify_mfma_kernel(VerifyArgs a) {
       if (r >= a.R) continue;
       const int hl = r / a.n_q, j = r % a.n_q;
       const size_t row = (size_t)(b * a.Hq + hk * a.g + hl) * a.n_q + j;
-      if (a.splits == 1) {
+      if (a.splits == 1 && !a.write_partials) {
         const float inv = le > 0.0f ? 1.0f / le : 0.0f;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) a.out[row * D + 16 * ct + col] = O[i][ct][e] * inv;
@@ -470,7 +472,8 @@ struct Plan {
 };
 
 // wpc: resident workgroups per CU of the kernel (8 bounds every variant).
-Plan plan_verify(int B, int Hq, int Hkv, int n_q, int max_ctx, int wpc) {
+// keys: length of the key range the call covers (max_ctx + n_q for a whole verify).
+Plan plan_verify(int B, int Hq, int Hkv, int n_q, int keys, int wpc) {
   Plan p{};
   const int g = Hq / Hkv;
   const int R = g * n_q;
@@ -483,7 +486,6 @@ Plan plan_verify(int B, int Hq, int Hkv, int n_q, int max_ctx, int wpc) {
   p.mt = (per_group + p.nw - 1) / p.nw;
   p.tiles_per_group = per_group;
   const int units = B * Hkv * p.rowgroups;
-  const int keys = max_ctx + n_q;
   const int target = wpc * num_cus();
   int s = target / units;
   const int cap = (keys + 4 * kKT - 1) / (4 * kKT);  // >= 4 tiles per split
@@ -502,43 +504,42 @@ size_t verify_ws_need(int B, int Hq, int n_q, int D, int splits) {
   return need < 256 ? 256 : need;
 }
 
-}  // namespace
-}  // namespace vc
+// Resident workgroups per CU the partial layout of a range call is planned
+// for: a fixed number per kernel shape (2 wavefronts per SIMD), so that
+// vc_verify_range_parts needs no device and always agrees with the call.
+int range_wpc(const Plan& p) { return p.nw == 2 * kWaves ? 1 : 2; }
 
-using namespace vc;
-
-extern "C" size_t vc_verify_ws_bytes(int B, int Hq, int Hkv, int D, int n_q, int max_ctx) {
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0 || n_q <= 0 || max_ctx < 0) return 0;
-  const Plan p = plan_verify(B, Hq, Hkv, n_q, max_ctx, 8);
-  return verify_ws_need(B, Hq, n_q, D, p.splits);
-}
-
-extern "C" int vc_verify_attn(const void* q, const vc_kv_full* kv, const int32_t* ctx_len, int max_ctx, int n_q,
-                              float* out, int B, int Hq, int Hkv, int D, float scale, void* ws, size_t ws_bytes,
-                              hipStream_t stream) {
-  VC_CHECK(q && kv && ctx_len && out, "vc_verify_attn: null q/kv/ctx_len/out");
-  VC_CHECK(B > 0 && Hq > 0 && Hkv > 0 && Hq % Hkv == 0, "vc_verify_attn: bad B/Hq/Hkv (%d,%d,%d)", B, Hq, Hkv);
-  if (D != 64 && D != 128) return fail(VC_ERR_UNSUPPORTED, "vc_verify_attn: D=%d not in {64,128}", D);
-  VC_CHECK(n_q >= 1 && max_ctx >= 0, "vc_verify_attn: n_q=%d max_ctx=%d", n_q, max_ctx);
-  VC_CHECK(aligned(q, 16) && aligned(out, 16), "vc_verify_attn: q/out must be 16-byte aligned");
+// Validates the arguments, plans and launches verify_mfma_kernel over keys
+// [key_begin, key_limit) of every sequence (clipped to ctx_len[b] + n_q).
+// parts != nullptr (a range call): the kernel writes its split partials there
+// and nothing else runs.  Otherwise the output goes to out, through the split
+// partials in ws and verify_combine_kernel when the keys are split.
+int verify_launch(const char* fn, const void* q, const vc_kv_full* kv, const int32_t* ctx_len, int max_ctx,
+                  int n_q, int key_begin, int key_limit, float* out, float* parts, int B, int Hq, int Hkv, int D,
+                  float scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+  VC_CHECK(q && kv && ctx_len && (out || parts), "%s: null q/kv/ctx_len/out", fn);
+  VC_CHECK(B > 0 && Hq > 0 && Hkv > 0 && Hq % Hkv == 0, "%s: bad B/Hq/Hkv (%d,%d,%d)", fn, B, Hq, Hkv);
+  if (D != 64 && D != 128) return fail(VC_ERR_UNSUPPORTED, "%s: D=%d not in {64,128}", fn, D);
+  VC_CHECK(n_q >= 1 && max_ctx >= 0, "%s: n_q=%d max_ctx=%d", fn, n_q, max_ctx);
+  VC_CHECK(aligned(q, 16) && (out == nullptr || aligned(out, 16)) && (parts == nullptr || aligned(parts, 16)),
+           "%s: q/out/parts must be 16-byte aligned", fn);
   VerifyArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(kv->k);
   a.v = static_cast<const uint16_t*>(kv->v);
-  VC_CHECK(kv->k != nullptr, "vc_verify_attn: null kv->k");
-  VC_CHECK(aligned(kv->k, 16), "vc_verify_attn: kv->k misaligned");
+  VC_CHECK(kv->k != nullptr, "%s: null kv->k", fn);
+  VC_CHECK(aligned(kv->k, 16), "%s: kv->k misaligned", fn);
   if (kv->page_table == nullptr) {
-    VC_CHECK(kv->v != nullptr && aligned(kv->v, 16), "vc_verify_attn: null or misaligned kv->v");
-    VC_CHECK((long long)max_ctx + n_q <= kv->L_cap, "vc_verify_attn: max_ctx + n_q = %d exceeds L_cap = %d",
+    VC_CHECK(kv->v != nullptr && aligned(kv->v, 16), "%s: null or misaligned kv->v", fn);
+    VC_CHECK((long long)max_ctx + n_q <= kv->L_cap, "%s: max_ctx + n_q = %d exceeds L_cap = %d", fn,
              max_ctx + n_q, kv->L_cap);
     a.L_cap = kv->L_cap;
   } else {
     const int pt = kv->page_tokens;
-    VC_CHECK(pt >= 8 && (pt & (pt - 1)) == 0, "vc_verify_attn: page_tokens=%d must be a power of two >= 8", pt);
+    VC_CHECK(pt >= 8 && (pt & (pt - 1)) == 0, "%s: page_tokens=%d must be a power of two >= 8", fn, pt);
     VC_CHECK((long long)kv->pages_per_seq * pt >= (long long)max_ctx + n_q,
-             "vc_verify_attn: %d pages of %d tokens cannot hold max_ctx + n_q = %d", kv->pages_per_seq, pt,
-             max_ctx + n_q);
-    VC_CHECK(kv->n_slots > 0, "vc_verify_attn: n_slots must be > 0");
+             "%s: %d pages of %d tokens cannot hold max_ctx + n_q = %d", fn, kv->pages_per_seq, pt, max_ctx + n_q);
+    VC_CHECK(kv->n_slots > 0, "%s: n_slots must be > 0", fn);
     a.page_table = kv->page_table;
     a.page_log2 = __builtin_ctz(pt);
     a.pages_per_seq = kv->pages_per_seq;
@@ -555,32 +556,90 @@ extern "C" int vc_verify_attn(const void* q, const vc_kv_full* kv, const int32_t
   a.R = a.g * n_q;
   a.NT = (a.R + 15) / 16;
   a.scale_log2 = scale * kLog2e;
-  Plan p = plan_verify(B, Hq, Hkv, n_q, max_ctx, 8);
+  a.key_begin = key_begin;
+  a.key_limit = key_limit;
+  a.write_partials = parts != nullptr ? 1 : 0;
+  const int keys = key_limit - key_begin;
+  Plan p = plan_verify(B, Hq, Hkv, n_q, keys, 8);
   const bool paged = kv->page_table != nullptr;
   const VerifyKernel kern = D == 128 ? (paged ? pick<128, true>(p.mt, p.nw) : pick<128, false>(p.mt, p.nw))
                                      : (paged ? pick<64, true>(p.mt, p.nw) : pick<64, false>(p.mt, p.nw));
-  p = plan_verify(B, Hq, Hkv, n_q, max_ctx, wgs_per_cu(kern, 64 * p.nw));
+  p = plan_verify(B, Hq, Hkv, n_q, keys, parts != nullptr ? range_wpc(p) : wgs_per_cu(kern, 64 * p.nw));
   a.rowgroups = p.rowgroups;
   a.tiles_per_group = p.tiles_per_group;
   a.splits = p.splits;
   a.keys_per_split = p.kps;
   a.n_su = p.splits * B * Hkv;
-  if (p.splits > 1) {
+  if (parts != nullptr) {
+    a.ws = parts;
+  } else if (p.splits > 1) {
     const size_t need = verify_ws_need(B, Hq, n_q, D, p.splits);
     if (ws == nullptr || ws_bytes < need)
-      return fail(VC_ERR_WORKSPACE, "vc_verify_attn: workspace %zu < %zu bytes", ws_bytes, need);
-    VC_CHECK(aligned(ws, 16), "vc_verify_attn: workspace misaligned");
-    VC_CHECK(p.splits <= kMaxCombineSplits, "vc_verify_attn: %d splits exceed %d", p.splits, kMaxCombineSplits);
+      return fail(VC_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+    VC_CHECK(aligned(ws, 16), "%s: workspace misaligned", fn);
+    VC_CHECK(p.splits <= kMaxCombineSplits, "%s: %d splits exceed %d", fn, p.splits, kMaxCombineSplits);
     a.ws = static_cast<float*>(ws);
   }
   // 1-D grid: 8 consecutive (split, unit) pairs per group of 8 * rowgroups workgroups
   const int n_wg = ((a.n_su + 7) / 8) * 8 * p.rowgroups;
   kern<<<n_wg, 64 * p.nw, 0, stream>>>(a);
   VC_HIP(hipGetLastError());
-  if (p.splits > 1) {
+  if (parts == nullptr && p.splits > 1) {
     const int rows = B * Hq * n_q;
     verify_combine_kernel<<<rows, 128, 0, stream>>>(a.ws, p.splits, rows, D, out);
     VC_HIP(hipGetLastError());
   }
+  return VC_OK;
+}
+
+}  // namespace
+}  // namespace vc
+
+using namespace vc;
+
+extern "C" size_t vc_verify_ws_bytes(int B, int Hq, int Hkv, int D, int n_q, int max_ctx) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0 || n_q <= 0 || max_ctx < 0) return 0;
+  const Plan p = plan_verify(B, Hq, Hkv, n_q, max_ctx + n_q, 8);
+  return verify_ws_need(B, Hq, n_q, D, p.splits);
+}
+
+extern "C" int vc_verify_attn(const void* q, const vc_kv_full* kv, const int32_t* ctx_len, int max_ctx, int n_q,
+                              float* out, int B, int Hq, int Hkv, int D, float scale, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  VC_CHECK(out != nullptr, "vc_verify_attn: null out");
+  return verify_launch("vc_verify_attn", q, kv, ctx_len, max_ctx, n_q, 0, max_ctx + n_q, out, nullptr, B, Hq, Hkv,
+                       D, scale, ws, ws_bytes, stream);
+}
+
+extern "C" int vc_verify_range_parts(int B, int Hq, int Hkv, int D, int n_q, int key_begin, int key_end) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || (D != 64 && D != 128) || n_q <= 0 || key_begin < 0 ||
+      key_end <= key_begin)
+    return 0;
+  const Plan p = plan_verify(B, Hq, Hkv, n_q, key_end - key_begin, 8);
+  return plan_verify(B, Hq, Hkv, n_q, key_end - key_begin, range_wpc(p)).splits;
+}
+
+extern "C" int vc_verify_attn_range(const void* q, const vc_kv_full* kv, const int32_t* ctx_len, int max_ctx,
+                                    int n_q, int key_begin, int key_end, float* parts, int B, int Hq, int Hkv, int D,
+                                    float scale, hipStream_t stream) {
+  VC_CHECK(parts != nullptr, "vc_verify_attn_range: null parts");
+  VC_CHECK(key_begin >= 0 && key_end > key_begin && key_end <= max_ctx + n_q,
+           "vc_verify_attn_range: key range [%d, %d) outside [0, max_ctx + n_q = %d)", key_begin, key_end,
+           max_ctx + n_q);
+  return verify_launch("vc_verify_attn_range", q, kv, ctx_len, max_ctx, n_q, key_begin, key_end, nullptr, parts, B,
+                       Hq, Hkv, D, scale, nullptr, 0, stream);
+}
+
+extern "C" int vc_verify_merge(const float* parts, int n_parts, int B, int Hq, int n_q, int D, float* out,
+                               hipStream_t stream) {
+  VC_CHECK(parts != nullptr && out != nullptr, "vc_verify_merge: null parts/out");
+  VC_CHECK(B > 0 && Hq > 0 && n_q > 0 && (D == 64 || D == 128), "vc_verify_merge: bad B/Hq/n_q/D (%d,%d,%d,%d)", B,
+           Hq, n_q, D);
+  VC_CHECK(n_parts >= 1 && n_parts <= kMaxCombineSplits, "vc_verify_merge: n_parts=%d outside [1, %d]", n_parts,
+           kMaxCombineSplits);
+  VC_CHECK(aligned(parts, 16) && aligned(out, 16), "vc_verify_merge: parts/out must be 16-byte aligned");
+  const int rows = B * Hq * n_q;
+  verify_combine_kernel<<<rows, 128, 0, stream>>>(parts, n_parts, rows, D, out);
+  VC_HIP(hipGetLastError());
   return VC_OK;
 }

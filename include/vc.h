@@ -207,6 +207,38 @@ int vc_verify_attn(const void* q, const vc_kv_full* kv, const int32_t* ctx_len, 
                    size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Chunked verify: the same attention as vc_verify_attn, taken one key range
+ * at a time, so that a caller can verify each chunk of a full cache as it
+ * arrives from host memory and merge at the end.  [VC Key System Innovations
+ * P1: the full KV is loaded over the interconnect while compute proceeds;
+ * VC Architecture Support: long-context decoding keeps the full KV in CPU
+ * memory]
+ *
+ * vc_verify_attn_range — keys [key_begin, key_end) of every sequence, clipped
+ * to the causal limit ctx_len[b] + j of query position j.  Arguments as in
+ * vc_verify_attn; only the pages (or rows) of the range are read, so the
+ * rest of a paged cache may still be in flight.  Writes
+ * vc_verify_range_parts(B, Hq, Hkv, D, n_q, key_begin, key_end) partial
+ * slots to parts (device fp32, 16-byte aligned), each [B*Hq*n_q][D + 2]:
+ * per query row the unnormalised sum o[0..D) of 2^(s - m) v over its keys,
+ * the score maximum m (log2 units of scale * q.k) and the sum l of 2^(s - m);
+ * m = -inf and l = 0 for a row that saw no key.  No output, no workspace.
+ * 0 <= key_begin < key_end <= max_ctx + n_q.
+ *
+ * vc_verify_merge — out[r] = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p
+ * with M = max_p m_p over n_parts (1..256) consecutive partial slots; rows
+ * = B*Hq*n_q, out device fp32 [rows][D].  A row no part saw gets 0.  Merging
+ * the parts of ranges that tile [0, max_ctx + n_q) gives vc_verify_attn's
+ * result up to rounding order.
+ */
+int vc_verify_range_parts(int B, int Hq, int Hkv, int D, int n_q, int key_begin, int key_end);
+int vc_verify_attn_range(const void* q, const vc_kv_full* kv, const int32_t* ctx_len, int max_ctx,
+                         int n_q, int key_begin, int key_end, float* parts, int B, int Hq, int Hkv, int D,
+                         float scale, hipStream_t stream);
+int vc_verify_merge(const float* parts, int n_parts, int B, int Hq, int n_q, int D, float* out,
+                    hipStream_t stream);
+
+/*
  * vc_argmax — greedy token of each row: ids[r] = index of the largest of
  * logits[r][0..V) (device fp32 [rows][V]); ties go to the lowest index.
  * Rows containing NaN give an unspecified index in [0, V).

@@ -61,6 +61,19 @@ def test_host_validation_without_gpu(lib):
     h = lib.vc_accept
     h.restype = ctypes.c_int
     assert h(None, None, 1, 2, 3, None, None, None) == -1
+    # chunked verify: the slot count is a host-side plan (deterministic, positive
+    # for a valid range, 0 otherwise); the range and merge calls reject bad input
+    rp = lib.vc_verify_range_parts
+    rp.restype = ctypes.c_int
+    n = rp(8, 64, 8, 128, 33, 0, 4096)
+    assert n >= 1 and n == rp(8, 64, 8, 128, 33, 0, 4096)
+    assert rp(8, 64, 8, 128, 33, 4096, 4096) == 0 and rp(8, 64, 8, 96, 33, 0, 4096) == 0
+    r = lib.vc_verify_attn_range
+    r.restype = ctypes.c_int
+    assert r(None, None, None, 4096, 33, 0, 4096, None, 8, 64, 8, 128, ctypes.c_float(0.088), None) == -1
+    m = lib.vc_verify_merge
+    m.restype = ctypes.c_int
+    assert m(None, 0, 8, 64, 33, 128, None, None) == -1
 
 
 def test_no_oracle_in_product_path():

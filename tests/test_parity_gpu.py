@@ -228,6 +228,85 @@ def test_verify_ragged_context_lengths():
             assert_close(got[b, h * g:(h + 1) * g], ref, f"ragged ctx b{b} h{h}")
 
 
+CHUNK_CASES = [
+    (C.TINY.with_(name="chunk_d128_g8_k32", B=2, Hq=16, Hkv=2, D=128, L=2085, k=32, seed=44), [517, 1500]),
+    (C.TINY.with_(name="chunk_paged_d128_g8", B=2, Hq=16, Hkv=2, D=128, L=1200, k=32, paged=True, page_tokens=16,
+                  seed=45), [256, 512, 768, 1024]),
+    (C.TINY.with_(name="chunk_d64_g4_k3", B=3, Hq=8, Hkv=2, D=64, L=97, k=3, seed=46), [40]),
+]
+
+
+@pytest.mark.parametrize("w,cuts", CHUNK_CASES, ids=[c[0].name for c in CHUNK_CASES])
+def test_verify_chunked_ranges_merge(w, cuts):
+    """Verify taken one key range at a time (as chunks of a full cache arrive)
+    and merged equals the causal verify of the oracle; the ranges end at the
+    context and the new rows form a range of their own."""
+    import torch
+    vc = _vc()
+    from compressed_kv_draft_amd.workload import DeviceWorkload
+    print(f"[case] chunked verify {w.name} cuts={cuts}", flush=True)
+    w = w.with_(kind="identity")
+    dw = DeviceWorkload(w, with_vocab=False)
+    edges = [0] + list(cuts) + [w.L, w.L + w.n_q]
+    B, Hq, n_q, D = dw.q_verify.shape
+    slots = [vc.verify_range_parts(B, Hq, w.Hkv, D, n_q, a, b) for a, b in zip(edges[:-1], edges[1:])]
+    rows = B * Hq * n_q * (D + 2)
+    parts = torch.full((sum(slots) * rows,), float("nan"), dtype=torch.float32, device="cuda")
+    off = 0
+    for (a, b), n in zip(zip(edges[:-1], edges[1:]), slots):
+        got_n = vc.verify_attn_range(dw.q_verify, dw.full, dw.ctx_len, w.L, w.Hkv, dw.scale, a, b,
+                                     parts[off * rows:])
+        assert got_n == n
+        off += n
+    got = vc.verify_merge(parts, sum(slots), B, Hq, n_q, D).cpu().numpy()
+    g = w.g
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            ref = R.unit_verify(w, dw.np["K"][b, h], dw.np["V"][b, h], dw.np["Kn"][b, h], dw.np["Vn"][b, h],
+                                dw.np["Q"][b, h * g:(h + 1) * g])
+            assert_close(got[b, h * g:(h + 1) * g], ref, f"{w.name} b{b} h{h}")
+
+
+def test_verify_chunked_ragged_context():
+    """Ranges past a sequence's ctx_len + n_q leave it untouched (empty partials),
+    and cache rows after that limit never leak in."""
+    import torch
+    vc = _vc()
+    from compressed_kv_draft_amd.workload import bf16_dev
+    from synth.gen import f32_to_bf16_bits
+    print("[case] chunked verify ragged ctx_len", flush=True)
+    rng = np.random.default_rng(12)
+    B, Hq, Hkv, D, n_q, L_cap = 3, 16, 2, 128, 33, 900
+    ctx = [800, 331, 5]
+    k = rng.standard_normal((B, Hkv, L_cap, D)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, L_cap, D)).astype(np.float32)
+    for b in range(B):
+        k[b, :, ctx[b] + n_q:] = 40.0
+        v[b, :, ctx[b] + n_q:] = 1000.0
+    q = rng.standard_normal((B, Hq, n_q, D)).astype(np.float32)
+    kb, vb, qb = (f32_to_bf16_bits(x) for x in (k, v, q))
+    full = vc.FullKV(bf16_dev(kb, "cuda"), bf16_dev(vb, "cuda"), L_cap=L_cap)
+    ctx_t = torch.tensor(ctx, dtype=torch.int32, device="cuda")
+    scale = O.scale_for(D)
+    qd = bf16_dev(qb, "cuda")
+    edges = [0, 300, 600, max(ctx) + n_q]
+    slots = [vc.verify_range_parts(B, Hq, Hkv, D, n_q, a, b) for a, b in zip(edges[:-1], edges[1:])]
+    rows = B * Hq * n_q * (D + 2)
+    parts = torch.empty((sum(slots) * rows,), dtype=torch.float32, device="cuda")
+    off = 0
+    for (a, b), n in zip(zip(edges[:-1], edges[1:]), slots):
+        vc.verify_attn_range(qd, full, ctx_t, max(ctx), Hkv, scale, a, b, parts[off * rows:])
+        off += n
+    got = vc.verify_merge(parts, sum(slots), B, Hq, n_q, D).cpu().numpy()
+    g = Hq // Hkv
+    for b in range(B):
+        n = ctx[b] + n_q
+        for h in range(Hkv):
+            ref = O.verify_attention_unit(O.bf16_to_f64(qb[b, h * g:(h + 1) * g]), O.bf16_to_f64(kb[b, h, :n]),
+                                          O.bf16_to_f64(vb[b, h, :n]), ctx[b], scale)
+            assert_close(got[b, h * g:(h + 1) * g], ref, f"chunked ragged b{b} h{h}")
+
+
 @pytest.mark.parametrize("bits", [2, 4])
 def test_draft_ragged_tail_lengths(bits):
     """Each sequence has its own exact-tail length (0 included): the rows past a
