@@ -51,7 +51,14 @@ def stagger(a):
     """Cross-resource staggering on one GPU: group B's full KV (shuffled 16-token
     pages, pinned host pool) streams to the device pool on a copy stream while
     group A runs its k draft steps on the compute stream.  Times draft alone,
-    copy alone and both together; overlap = (t_d + t_c - t_both) / min(t_d, t_c)."""
+    copy alone and both together; overlap = 1 - (t_both - t_copy) / min(t_d, t_c), the
+    difference taken over paired runs.
+    Then group B's verify: once after all its chunks have landed, and chunk by
+    chunk (vc_verify_attn_range on each 4096-key chunk as soon as it lands, the
+    new rows as one more range, then vc_verify_merge).  The verify's tail is the
+    GPU time from the last chunk landing to the verified output: after the whole
+    copy it is the whole verify; chunk by chunk it is one chunk's share plus the
+    new rows and the merge.  Hidden share = 1 - tail / t_verify."""
     import numpy as np
     import torch
 
@@ -77,11 +84,29 @@ def stagger(a):
     n_pages = pages_per_chunk * len(chunks)
     copy_bytes = n_pages * page_bytes
     chunk_bytes = pages_per_chunk * page_bytes
-    # group B's device region: its chunks one after the other (a device page
-    # table for the paged verify points here)
-    dev_region = torch.empty(copy_bytes, dtype=torch.uint8, device="cuda:0")
-    staging = [torch.empty(chunk_bytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
-    done = [torch.cuda.Event(), torch.cuda.Event()]
+    # group B's device pool: its chunks one after the other, then the pages of
+    # the new rows (device-only); a device page table points the paged verify here
+    ctx_pages = w.L // w.page_tokens
+    pps = table.shape[1]
+    extra = pps - ctx_pages
+    seq_chunk_pages = w.chunk_tokens // w.page_tokens
+    pool_b = torch.empty((n_pages + bg * extra) * page_bytes, dtype=torch.uint8, device="cuda:0")
+    pool_b[copy_bytes:].fill_(0x3C)
+    dev_region = pool_b[:copy_bytes]
+    tab_b = np.empty((bg, pps), dtype=np.int32)
+    for i in range(bg):
+        p = np.arange(ctx_pages)
+        tab_b[i, :ctx_pages] = (p // seq_chunk_pages) * pages_per_chunk + i * seq_chunk_pages + p % seq_chunk_pages
+        tab_b[i, ctx_pages:] = n_pages + i * extra + np.arange(extra)
+    full_b = vc.FullKV(pool_b, None, 0, torch.from_numpy(tab_b).to("cuda:0"), w.page_tokens, pps,
+                       n_pages + bg * extra)
+    q_b = torch.randn((bg, w.Hq, w.n_q, w.D), device="cuda:0").to(torch.bfloat16)
+    ctx_b = torch.full((bg,), w.L, dtype=torch.int32, device="cuda:0")
+    scale = float(np.float32(1.0 / np.sqrt(w.D)))
+    # three staging buffers: the gather of chunk c waits only for the copy of c - 3
+    n_stage = 3
+    staging = [torch.empty(chunk_bytes, dtype=torch.uint8, pin_memory=True) for _ in range(n_stage)]
+    landed = [torch.cuda.Event() for _ in chunks]     # chunk c is on the device
     comp = torch.cuda.current_stream()
     cps = torch.cuda.Stream()
 
@@ -89,11 +114,15 @@ def stagger(a):
         for j in range(w.k):
             dw.draft_step(j)
 
+    def copy_chunk(c):
+        t0, t1 = chunks[c]
+        vc.prefetch_full_kv(host, page_bytes, table, seqs, t0, t1, w.page_tokens, staging[c % n_stage],
+                            dev_region[c * chunk_bytes:(c + 1) * chunk_bytes], stream=cps, done_event=landed[c],
+                            staging_free=landed[c - n_stage] if c >= n_stage else None)
+
     def copies():
-        for c, (t0, t1) in enumerate(chunks):
-            vc.prefetch_full_kv(host, page_bytes, table, seqs, t0, t1, w.page_tokens, staging[c % 2],
-                                dev_region[c * chunk_bytes:(c + 1) * chunk_bytes], stream=cps,
-                                done_event=done[c % 2], staging_free=done[c % 2] if c >= 2 else None)
+        for c in range(len(chunks)):
+            copy_chunk(c)
 
     def timed(fn, stream):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -132,8 +161,11 @@ def stagger(a):
     tref = float(np.median([timed(lambda: dev_region[:chunk_bytes].copy_(big, non_blocking=True), comp)[0]
                             for _ in range(reps)]))
     import threading
-    both, d_in = [], []
+    # copy alone and copy + drafts alternate, so that the slow drift of the PCIe
+    # rate (a few ms over a 40 ms copy) cancels in the paired differences
+    both, d_in, alone = [], [], []
     for _ in range(reps):
+        alone.append(timed(copies, cps)[1])
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         # the prefetch runs on its own host thread (its gathers and copy submissions
@@ -150,7 +182,68 @@ def stagger(a):
         d_in.append(dA0.elapsed_time(dA1))
     tb = float(np.median(both))
     tdi = float(np.median(d_in))
-    overlap = (td + tc - tb) / min(td, tc)
+    extra = float(np.median(np.array(both) - np.array(alone)))   # what the drafts added to the copy
+    overlap = (min(td, tc) - extra) / min(td, tc)
+
+    # group B's verify: whole, after all chunks; and chunk by chunk as they land
+    ranges = chunks + [(w.L, w.L + w.n_q)]
+    slots = [vc.verify_range_parts(bg, w.Hq, w.Hkv, w.D, w.n_q, t0, t1) for t0, t1 in ranges]
+    row_f = bg * w.Hq * w.n_q * (w.D + 2)
+    parts = torch.empty(sum(slots) * row_f, dtype=torch.float32, device="cuda:0")
+    out_whole = torch.empty((bg, w.Hq, w.n_q, w.D), dtype=torch.float32, device="cuda:0")
+    out_pipe = torch.empty_like(out_whole)
+    last_landed = torch.cuda.Event(enable_timing=True)
+    merged = torch.cuda.Event(enable_timing=True)
+
+    def verify_whole():
+        vc.verify_attn(q_b, full_b, ctx_b, w.L, w.Hkv, scale, out=out_whole)
+
+    def copies_flagged(flags):
+        for c in range(len(chunks)):
+            copy_chunk(c)
+            if c == len(chunks) - 1:
+                last_landed.record(cps)
+            flags[c].set()
+
+    def pipelined():
+        flags = [threading.Event() for _ in chunks]
+        th = threading.Thread(target=copies_flagged, args=(flags,))
+        th.start()
+        off = 0
+        for c, ((t0, t1), n) in enumerate(zip(ranges, slots)):
+            if c < len(chunks):
+                flags[c].wait()             # the chunk's copy (and its event) is enqueued
+                comp.wait_event(landed[c])  # ... and the verify of its keys waits for it to land
+            vc.verify_attn_range(q_b, full_b, ctx_b, w.L, w.Hkv, scale, t0, t1, parts[off * row_f:])
+            off += n
+        vc.verify_merge(parts, sum(slots), bg, w.Hq, w.n_q, w.D, out=out_pipe)
+        merged.record(comp)
+        th.join()
+
+    copies()
+    torch.cuda.synchronize()
+    verify_whole()
+    pipelined()
+    torch.cuda.synchronize()
+    rel = float(torch.linalg.norm(out_pipe - out_whole) / torch.linalg.norm(out_whole))
+    if not rel < 1e-5:
+        raise RuntimeError(f"chunked verify differs from the whole verify: rel L2 {rel:.2e}")
+    tv = float(np.median([timed(verify_whole, comp)[0] for _ in range(reps)]))
+    serial, pipe, tails = [], [], []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        copies()
+        comp.wait_stream(cps)
+        verify_whole()
+        torch.cuda.synchronize()
+        serial.append(1e3 * (time.perf_counter() - t0))
+        t0 = time.perf_counter()
+        pipelined()
+        torch.cuda.synchronize()
+        pipe.append(1e3 * (time.perf_counter() - t0))
+        tails.append(last_landed.elapsed_time(merged))
+    ts, tp, tt = float(np.median(serial)), float(np.median(pipe)), float(np.median(tails))
     line = {"metric": "full-KV prefetch overlap with draft compute (cross-resource staggering, one GPU)",
             "value": round(overlap, 4), "unit": "fraction of the shorter activity hidden", "n_gpus": 1,
             "steps": reps, "higher_is_better": True, "data": "synthetic",
@@ -158,6 +251,11 @@ def stagger(a):
                        "prefetch_group": f"seqs {bg}..{2 * bg - 1}, {len(chunks)} chunks of {w.chunk_tokens} "
                                          f"tokens, {n_pages} shuffled pages of {page_bytes} B"},
             "t_draft_ms": round(td, 3), "t_copy_ms": round(tc, 3), "t_both_ms": round(tb, 3),
+            "verify_ms": round(tv, 3), "copy_then_verify_ms": round(ts, 3), "chunked_verify_ms": round(tp, 3),
+            "chunked_verify_tail_ms": round(tt, 3), "verify_hidden_fraction": round(1.0 - tt / tv, 4),
+            "chunked_vs_whole_rel_l2": rel,
+            "chunked_verify": f"{len(chunks)} ranges of {w.chunk_tokens} keys as they land + new rows + merge, "
+                              f"{sum(slots)} partial slots",
             "draft_under_copy_ms": round(tdi, 3), "draft_slowdown": round(tdi / td, 4),
             "prefetch_GBps": round(copy_bytes / tc / 1e6, 2),
             "pcie_GBps_one_chunk_copy": round(chunk_bytes / tref / 1e6, 2),

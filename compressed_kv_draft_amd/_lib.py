@@ -295,9 +295,14 @@ def prefetch_full_kv(host_pool: torch.Tensor, page_bytes: int, page_table_host, 
     need = len(seqs) * (p1 - p0) * page_bytes
     if dev_dst.numel() < need:
         raise VcError(f"dev_dst holds {dev_dst.numel()} bytes < {need}")
-    ev = c_void(done_event.cuda_event) if done_event is not None else None
-    fr = c_void(staging_free.cuda_event) if staging_free is not None else None
     s = torch.cuda.current_stream() if stream is None else stream
+    # torch creates an event's HIP handle at its first record; record `done_event`
+    # on the copy stream first so that it has one for the library to record after
+    # the copy (an unrecorded `staging_free` has nothing to wait for: NULL)
+    if done_event is not None and not done_event.cuda_event:
+        done_event.record(s)
+    ev = c_void(done_event.cuda_event) if done_event is not None else None
+    fr = c_void(staging_free.cuda_event) if staging_free is not None and staging_free.cuda_event else None
     rc = LIB.vc_prefetch_full_kv(c_void(host_pool.data_ptr()), page_bytes, n_slots, tab.ctypes.data_as(c_void),
                                  tab.shape[0], tab.shape[1], seqs.ctypes.data_as(c_void), len(seqs), tok_begin,
                                  tok_end, page_tokens, c_void(staging.data_ptr()), staging.numel(),
