@@ -312,6 +312,25 @@ def accept(draft_ids: np.ndarray, verify_tokens: np.ndarray):
 
 
 # ----------------------------------------------------------------------------
+# token selection  [VC Problem Statement: token dropping keeps part of the
+# context's tokens; VC Architecture Support: token-dropping compressors behind
+# the uniform interface.  The pages describe no selection rule; the reading
+# here keeps the M tokens of highest importance score per (batch, kv-head)]
+# ----------------------------------------------------------------------------
+
+
+def select_top_m(scores: np.ndarray, M: int) -> np.ndarray:
+    """Indices of the M largest scores of one (batch, kv-head) row, ties broken
+    toward the lower index, returned in ascending index order (the kept-row list
+    the token-dropped draft gathers).  Scores compare as real numbers (-0 == +0);
+    NaN is not allowed.  0 <= M <= len(scores)."""
+    s = np.asarray(scores, dtype=np.float64)
+    assert 0 <= M <= len(s) and not np.isnan(s).any()
+    order = np.lexsort((np.arange(len(s)), -s))   # score descending, then index ascending
+    return np.sort(order[:M]).astype(np.int32)
+
+
+# ----------------------------------------------------------------------------
 # full-KV prefetch  [VC Architecture Support, long-context decoding: compressed
 # KV in HBM, full KV in CPU memory loaded over PCIe for verification; VC Key
 # System Innovations P1: the load overlaps other requests' drafting]

@@ -468,3 +468,73 @@ def test_pins_catch_planted_mistakes():
         pin_quant_brute_force(quant_floor, _dequant_groups, 4, ngroups=50)
     with pytest.raises(AssertionError):
         pin_quant_brute_force(O.quantize_groups, dequant_swapped, 4, ngroups=50)
+
+
+# ---------------------------------------------------------------------------
+# token selection: the defining property of the kept set, checked directly
+
+
+def pin_select_top_m(select):
+    """The kept set S (|S| = M) is defined by: every kept score >= every dropped
+    score (as real numbers), and at the boundary value v = min kept score every
+    kept index with score v is lower than every dropped index with score v; the
+    list is ascending.  Checked on random rows with heavy ties, signed zeros and
+    infinities, plus closed cases."""
+    rng = np.random.default_rng(17)
+    pool = np.array([-np.inf, -2.5, -0.0, 0.0, 0.75, 0.75, 3.0, np.inf])
+    for trial in range(300):
+        L = int(rng.integers(1, 40))
+        s = pool[rng.integers(0, len(pool), L)] if trial % 2 else rng.standard_normal(L).round(1)
+        M = int(rng.integers(0, L + 1))
+        got = np.asarray(select(s, M))
+        assert got.shape == (M,) and got.dtype == np.int32, (trial, got)
+        assert np.all(np.diff(got) > 0), ("ascending, unique", trial, got)
+        if M == 0:
+            continue
+        kept = np.zeros(L, bool)
+        kept[got] = True
+        ks, ds = s[kept], s[~kept]
+        if ds.size:
+            assert ks.min() >= ds.max(), ("kept >= dropped", trial, s, got)
+            v = ks.min()
+            ki = np.flatnonzero(kept & (s == v))
+            di = np.flatnonzero(~kept & (s == v))
+            if di.size:
+                assert ki.max() < di.min(), ("ties to the lower index", trial, s, got)
+    # closed cases
+    s = np.array([0.5, 2.0, -1.0, 2.0, 0.5, 7.0])
+    assert list(select(s, 3)) == [1, 3, 5]
+    assert list(select(s, 4)) == [0, 1, 3, 5]
+    assert list(select(s, 0)) == []
+    assert list(select(s, 6)) == [0, 1, 2, 3, 4, 5]
+    assert list(select(np.zeros(9), 4)) == [0, 1, 2, 3]
+    assert list(select(np.array([0.0, -0.0, 0.0]), 2)) == [0, 1]
+
+
+def test_select_top_m_pins():
+    pin_select_top_m(O.select_top_m)
+
+
+def test_select_pins_catch_planted_mistakes():
+    def ties_high(s, M):
+        s = np.asarray(s, np.float64)
+        order = np.lexsort((-np.arange(len(s)), -s))
+        return np.sort(order[:M]).astype(np.int32)
+
+    def unsorted(s, M):
+        s = np.asarray(s, np.float64)
+        return np.lexsort((np.arange(len(s)), -s))[:M].astype(np.int32)
+
+    def bottom_m(s, M):
+        s = np.asarray(s, np.float64)
+        return np.sort(np.lexsort((np.arange(len(s)), s))[:M]).astype(np.int32)
+
+    def signed_zero_order(s, M):
+        # orders -0 below +0 (bit patterns instead of values)
+        s = np.asarray(s, np.float64)
+        key = s + np.where(np.signbit(s) & (s == 0), -1e-300, 0.0)
+        return np.sort(np.lexsort((np.arange(len(s)), -key))[:M]).astype(np.int32)
+
+    for bad in (ties_high, unsorted, bottom_m, signed_zero_order):
+        with pytest.raises(AssertionError):
+            pin_select_top_m(bad)
