@@ -43,6 +43,7 @@ EXPORTS = {
     "vc_version": (c_int, []),
     "vc_last_error": (ctypes.c_char_p, []),
     "vc_quantize_kv": (c_int, [c_void, c_void, c_int, c_int, c_int, c_int, ctypes.POINTER(VcKvComp), c_void]),
+    "vc_select_top_m": (c_int, [c_void, c_int, c_int, c_int, c_void, c_void]),
     "vc_debug_dequant": (c_int, [ctypes.POINTER(VcKvComp), c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void]),
     "vc_draft_ws_bytes": (c_size, [c_int, c_int, c_int, c_int, c_int]),
     "vc_draft_attn": (c_int, [ctypes.POINTER(VcKvComp), ctypes.POINTER(VcTail), c_void, c_void, c_void,
@@ -165,6 +166,19 @@ class Tail:
         else:
             d.T_cap = 0
         self.desc = d
+
+
+def select_top_m(scores: torch.Tensor, M: int, keep_idx=None, stream=None) -> torch.Tensor:
+    """scores: fp32 [..., L] (one row per (batch, kv-head)).  Returns int32 [..., M]:
+    the indices of the M largest scores of each row, ties to the lower index, ascending."""
+    L = scores.shape[-1]
+    rows = scores.numel() // L if L else 0
+    if scores.dtype != torch.float32 or not scores.is_contiguous():
+        raise VcError("vc_select_top_m: scores must be contiguous fp32")
+    if keep_idx is None:
+        keep_idx = torch.empty((*scores.shape[:-1], M), dtype=torch.int32, device=scores.device)
+    _check(LIB.vc_select_top_m(_ptr(scores), rows, L, int(M), _ptr(keep_idx), _stream(stream)), "vc_select_top_m")
+    return keep_idx
 
 
 def draft_ws_bytes(B, Hq, Hkv, D, max_keys) -> int:

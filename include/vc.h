@@ -154,6 +154,18 @@ int vc_quantize_kv(const void* k_src, const void* v_src, int B, int Hkv, int L_c
                    const vc_kv_comp* out, hipStream_t stream);
 
 /*
+ * vc_select_top_m — the token-dropping compressor's selection: for each of
+ * `rows` rows (one per (batch, kv-head)) of importance scores (device fp32
+ * [rows][L]), keep_idx[r] (device int32 [rows][M]) receives the indices of
+ * the M largest scores, ties to the lower index, in ascending order: the
+ * kept-row list of a VC_KV_TOKEN_DROP cache.  Scores compare as numbers (-0
+ * equals +0); NaN scores give an unspecified (but valid, sorted, unique) set.
+ * 0 <= M <= L.  [VC Problem Statement: token dropping; VC Architecture
+ * Support: token-dropping compressors behind the uniform interface]
+ */
+int vc_select_top_m(const float* scores, int rows, int L, int M, int32_t* keep_idx, hipStream_t stream);
+
+/*
  * vc_debug_dequant — dequantised K (which = 0) or V (which = 1) of one
  * (b, kv-head) as fp32 [n_quant][D] into out (device).  For bit-exact checks.
  */

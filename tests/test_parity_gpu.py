@@ -307,6 +307,40 @@ def test_verify_chunked_ragged_context():
             assert_close(got[b, h * g:(h + 1) * g], ref, f"chunked ragged b{b} h{h}")
 
 
+def _select_cases():
+    rng = np.random.default_rng(51)
+    pool = np.array([-np.inf, -2.5, -0.0, 0.0, 0.75, 3.0, np.inf], dtype=np.float32)
+    cases = [("qwen_32b_rows_u01", rng.random((32, 131072), dtype=np.float32), 13107)]
+    cases.append(("ties_signed_zero_inf", pool[rng.integers(0, len(pool), (6, 5000))], 1234))
+    for L, M in ((1, 1), (37, 1), (37, 36), (1023, 500), (1025, 1024), (3000, 2999), (2048, 1)):
+        cases.append((f"L{L}_M{M}", rng.standard_normal((3, L)).astype(np.float32).round(1), M))
+    cases.append(("all_equal", np.full((2, 4100), 0.5, np.float32), 4000))
+    cases.append(("M_eq_L", rng.random((2, 777), dtype=np.float32), 777))
+    return cases
+
+
+@pytest.mark.parametrize("name,scores,M", _select_cases(), ids=[c[0] for c in _select_cases()])
+def test_select_top_m_bit_exact(name, scores, M):
+    """The GPU top-M selector returns exactly the oracle's kept-index lists."""
+    import time
+    import torch
+    vc = _vc()
+    print(f"[case] select {name} rows={scores.shape[0]} L={scores.shape[1]} M={M}", flush=True)
+    sd = torch.from_numpy(np.ascontiguousarray(scores)).to("cuda")
+    got = vc.select_top_m(sd, M)
+    torch.cuda.synchronize()
+    if name.startswith("qwen"):
+        t0 = time.perf_counter()
+        for _ in range(5):
+            vc.select_top_m(sd, M, keep_idx=got)
+        torch.cuda.synchronize()
+        print(f"[time] select {name}: {(time.perf_counter() - t0) / 5 * 1e6:.1f} us per call", flush=True)
+    got = got.cpu().numpy()
+    for r in range(scores.shape[0]):
+        ref = O.select_top_m(scores[r], M)
+        assert np.array_equal(got[r], ref), (name, r, np.flatnonzero(got[r] != ref)[:5])
+
+
 @pytest.mark.parametrize("bits", [2, 4])
 def test_draft_ragged_tail_lengths(bits):
     """Each sequence has its own exact-tail length (0 included): the rows past a
