@@ -26,7 +26,7 @@ class VcKvComp(ctypes.Structure):
     _fields_ = [("kind", c_int), ("bits", c_int), ("n_quant", c_int),
                 ("k_codes", c_void), ("v_codes", c_void), ("k_meta", c_void), ("v_meta", c_void),
                 ("k_full", c_void), ("v_full", c_void), ("L_full", c_int), ("L_cap", c_int),
-                ("keep_idx", c_void), ("n_keep", c_int)]
+                ("keep_idx", c_void), ("n_keep", c_int), ("q_cap", c_int)]
 
 
 class VcTail(ctypes.Structure):
@@ -43,6 +43,8 @@ EXPORTS = {
     "vc_version": (c_int, []),
     "vc_last_error": (ctypes.c_char_p, []),
     "vc_quantize_kv": (c_int, [c_void, c_void, c_int, c_int, c_int, c_int, ctypes.POINTER(VcKvComp), c_void]),
+    "vc_quantize_blocks": (c_int, [c_void, c_void, c_int, c_int, c_int, c_int, c_int, c_int,
+                                   ctypes.POINTER(VcKvComp), c_int, c_void]),
     "vc_select_top_m": (c_int, [c_void, c_int, c_int, c_int, c_void, c_void]),
     "vc_debug_dequant": (c_int, [ctypes.POINTER(VcKvComp), c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void]),
     "vc_draft_ws_bytes": (c_size, [c_int, c_int, c_int, c_int, c_int]),
@@ -117,23 +119,55 @@ class Compressed:
         d.L_full = int(t.get("L_full", 0))
         d.L_cap = int(t.get("L_cap", 0))
         d.n_keep = int(t.get("n_keep", 0))
+        d.q_cap = int(t.get("q_cap", 0))
         self.desc = d
 
+    def set_n_quant(self, n: int):
+        """Live quantised rows of a QUANT cache (after blocks were appended)."""
+        cap = self.desc.q_cap or self.desc.n_quant
+        if n % 32 or not 0 <= n <= cap:
+            raise VcError(f"n_quant={n} must be a multiple of 32 in [0, {cap}]")
+        self.t["n_quant"] = n
+        self.desc.n_quant = n
 
-def quantize_kv(k_src: torch.Tensor, v_src: torch.Tensor, bits: int, n_quant: int, stream=None) -> Compressed:
-    """k_src/v_src: bf16 [B, Hkv, L_cap, D] on the device.  Returns the QUANT cache."""
+
+def quantize_kv(k_src: torch.Tensor, v_src: torch.Tensor, bits: int, n_quant: int, stream=None,
+                capacity: int | None = None) -> Compressed:
+    """k_src/v_src: bf16 [B, Hkv, L_cap, D] on the device.  Returns the QUANT cache of
+    rows [0, n_quant), in arrays that hold `capacity` rows (default n_quant) so that
+    quantize_blocks can grow it."""
     B, Hkv, L_cap, D = k_src.shape
     dev = k_src.device
     rb = D * bits // 8
-    t = dict(bits=bits, n_quant=n_quant,
-             k_codes=torch.empty((B, Hkv, n_quant, rb), dtype=torch.uint8, device=dev),
-             v_codes=torch.empty((B, Hkv, n_quant, rb), dtype=torch.uint8, device=dev),
-             k_meta=torch.empty((B, Hkv, n_quant // 32, 2, D), dtype=torch.float16, device=dev),
-             v_meta=torch.empty((B, Hkv, n_quant // 32, D // 32, 32, 2), dtype=torch.float16, device=dev))
+    cap = n_quant if capacity is None else int(capacity)
+    if cap % 32 or cap < n_quant:
+        raise VcError(f"capacity={cap} must be a multiple of 32 and >= n_quant={n_quant}")
+    t = dict(bits=bits, n_quant=n_quant, q_cap=cap,
+             k_codes=torch.empty((B, Hkv, cap, rb), dtype=torch.uint8, device=dev),
+             v_codes=torch.empty((B, Hkv, cap, rb), dtype=torch.uint8, device=dev),
+             k_meta=torch.empty((B, Hkv, cap // 32, 2, D), dtype=torch.float16, device=dev),
+             v_meta=torch.empty((B, Hkv, cap // 32, D // 32, 32, 2), dtype=torch.float16, device=dev))
     comp = Compressed("quant", **t)
     rc = LIB.vc_quantize_kv(_ptr(k_src), _ptr(v_src), B, Hkv, L_cap, D, ctypes.byref(comp.desc), _stream(stream))
     _check(rc, "vc_quantize_kv")
     comp.t["src_keepalive"] = (k_src, v_src)
+    return comp
+
+
+def quantize_blocks(k_src: torch.Tensor, v_src: torch.Tensor, comp: Compressed, src_row0: int, n_blocks: int,
+                    dst_block: int | None = None, stream=None) -> Compressed:
+    """Quantise rows [src_row0, src_row0 + 32 n_blocks) of k_src/v_src (bf16 [B, Hkv, rows, D])
+    into blocks [dst_block, dst_block + n_blocks) of comp.  dst_block None appends after
+    the live rows and raises comp's n_quant by 32 n_blocks."""
+    B, Hkv, rows, D = k_src.shape
+    append = dst_block is None
+    if append:
+        dst_block = comp.desc.n_quant // 32
+    rc = LIB.vc_quantize_blocks(_ptr(k_src), _ptr(v_src), B, Hkv, rows, D, int(src_row0), int(n_blocks),
+                                ctypes.byref(comp.desc), int(dst_block), _stream(stream))
+    _check(rc, "vc_quantize_blocks")
+    if append:
+        comp.set_n_quant(comp.desc.n_quant + 32 * n_blocks)
     return comp
 
 

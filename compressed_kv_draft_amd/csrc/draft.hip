@@ -39,7 +39,7 @@ namespace {
 
 struct DraftArgs {
   int n_main;    // rows of the compressed part (quant: n_quant; identity: L_full; drop: n_keep)
-  int n_quant;
+  int q_cap;  // quant: rows per unit the code/meta arrays hold (their stride)
   int L_cap;
   int row_bound;  // valid physical rows of k_full/v_full (identity / drop)
   const uint8_t* k_codes;
@@ -524,7 +524,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
       // no registers hold data in flight, and the metadata arrive already in
       // the order the matrix-core operands read them.  All addressing of the
       // loads is wave-uniform (scalar registers) plus the lane's 16-byte offset.
-      const int nq32 = a.n_quant / 32;
+      const int nq32 = a.q_cap / 32;
       const int wave_u = __builtin_amdgcn_readfirstlane(wave);
       const unsigned char* kcodes = a.k_codes + unit_rows * nq32 * C::KC_BYTES;
       const unsigned char* vcodes = a.v_codes + unit_rows * nq32 * C::VC_BYTES;
@@ -846,8 +846,10 @@ extern "C" int vc_draft_attn(const vc_kv_comp* comp, const vc_tail* tail, const 
       VC_CHECK(aligned(comp->k_codes, 16) && aligned(comp->v_codes, 16) && aligned(comp->k_meta, 16) &&
                    aligned(comp->v_meta, 16),
                "vc_draft_attn: codes and meta must be 16-byte aligned");
+      VC_CHECK(quant_cap(comp) >= comp->n_quant && quant_cap(comp) % 32 == 0,
+               "vc_draft_attn: q_cap=%d below n_quant=%d or not a multiple of 32", comp->q_cap, comp->n_quant);
       bits = comp->bits;
-      a.n_quant = comp->n_quant;
+      a.q_cap = quant_cap(comp);
       a.n_main = comp->n_quant;
       a.k_codes = comp->k_codes;
       a.v_codes = comp->v_codes;

@@ -31,10 +31,15 @@ __device__ __forceinline__ uint32_t code_of(float x, float s, float z, int qmax)
   return (uint32_t)r;
 }
 
+// Every kernel below quantises source rows [32 i, 32 i + 32) of each (batch,
+// kv-head), i < n_blocks (src already points at the first row; rows are
+// src_cap apart per unit), into cache block blk0 + i of arrays that hold cap32
+// blocks per unit.
+//
 // K: groups of 32 tokens of one channel.  One thread per (32-token block, byte
 // column): it owns the 8/bits channels packed into that byte.
 template <int BITS>
-__global__ void quant_k_kernel(const uint16_t* __restrict__ src, int L_cap, int D, int n_quant,
+__global__ void quant_k_kernel(const uint16_t* __restrict__ src, int L_cap, int D, int blk0, int cap32,
                                uint8_t* __restrict__ codes, H2* __restrict__ meta) {
   constexpr int PER = 8 / BITS;
   constexpr int QMAX = (1 << BITS) - 1;
@@ -65,12 +70,12 @@ __global__ void quant_k_kernel(const uint16_t* __restrict__ src, int L_cap, int 
     const float s = (float)sh, z = (float)zh;
 #pragma unroll
     for (int i = 0; i < 32; ++i) packed[i] |= code_of(x[i], s, z, QMAX) << (BITS * e);
-    _Float16* plane = reinterpret_cast<_Float16*>(meta + ((size_t)unit * (n_quant / 32) + blk) * D);
+    _Float16* plane = reinterpret_cast<_Float16*>(meta + ((size_t)unit * cap32 + blk0 + blk) * D);
     const int pos = kmeta_pos(D, BITS, d);
     plane[pos] = sh;
     plane[D + pos] = zh;
   }
-  uint8_t* out = codes + ((size_t)unit * n_quant + (size_t)blk * 32) * row_bytes + col;
+  uint8_t* out = codes + ((size_t)unit * cap32 + blk0 + blk) * 32 * row_bytes + col;
 #pragma unroll
   for (int i = 0; i < 32; ++i) out[(size_t)i * row_bytes] = (uint8_t)packed[i];
 }
@@ -78,13 +83,13 @@ __global__ void quant_k_kernel(const uint16_t* __restrict__ src, int L_cap, int 
 // V: groups of 32 channels of one token.  Pass 1, one thread per (token, group):
 // the group's scale and zero.
 template <int BITS>
-__global__ void quant_v_meta_kernel(const uint16_t* __restrict__ src, int L_cap, int D, int n_quant,
-                                    H2* __restrict__ meta) {
+__global__ void quant_v_meta_kernel(const uint16_t* __restrict__ src, int L_cap, int D, int n_blocks, int blk0,
+                                    int cap32, H2* __restrict__ meta) {
   constexpr int QMAX = (1 << BITS) - 1;
   const int unit = blockIdx.y;
   const int G = D / 32;
   const int gid = blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= n_quant * G) return;
+  if (gid >= n_blocks * 32 * G) return;
   const int t = gid / G, grp = gid % G;
   const uint16_t* row = src + ((size_t)unit * L_cap + t) * D + grp * 32;
   float mn = bf16_to_f32(row[0]), mx = mn;
@@ -96,19 +101,19 @@ __global__ void quant_v_meta_kernel(const uint16_t* __restrict__ src, int L_cap,
   }
   H2 m;
   group_params(mn, mx, QMAX, m.s, m.z);
-  meta[(((size_t)unit * (n_quant / 32) + t / 32) * G + grp) * 32 + vmeta_slot(t % 32)] = m;
+  meta[(((size_t)unit * cap32 + blk0 + t / 32) * G + grp) * 32 + vmeta_slot(t % 32)] = m;
 }
 
 // V pass 2, one thread per code byte of the tiled layout (vc_vcode_locate in
 // vc_common.h): the byte's codes all belong to one token.
 template <int BITS>
-__global__ void quant_v_pack_kernel(const uint16_t* __restrict__ src, int L_cap, int D, int n_quant,
-                                    const H2* __restrict__ meta, uint8_t* __restrict__ codes) {
+__global__ void quant_v_pack_kernel(const uint16_t* __restrict__ src, int L_cap, int D, int n_blocks, int blk0,
+                                    int cap32, const H2* __restrict__ meta, uint8_t* __restrict__ codes) {
   constexpr int QMAX = (1 << BITS) - 1;
   const int unit = blockIdx.y;
   const int block_bytes = 4 * D * BITS;  // 32 tokens x D codes
   const int gid = blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (n_quant / 32) * block_bytes) return;
+  if (gid >= n_blocks * block_bytes) return;
   const int blk = gid / block_bytes, byte = gid % block_bytes;
   uint32_t v = 0;
 #pragma unroll
@@ -117,10 +122,10 @@ __global__ void quant_v_pack_kernel(const uint16_t* __restrict__ src, int L_cap,
     vcode_inverse(D, BITS, byte, k, tau, c);
     const int t = blk * 32 + tau;
     const float x = bf16_to_f32(src[((size_t)unit * L_cap + t) * D + c]);
-    const H2 m = meta[(((size_t)unit * (n_quant / 32) + t / 32) * (D / 32) + c / 32) * 32 + vmeta_slot(tau)];
+    const H2 m = meta[(((size_t)unit * cap32 + blk0 + blk) * (D / 32) + c / 32) * 32 + vmeta_slot(tau)];
     v |= code_of(x, (float)m.s, (float)m.z, QMAX) << (BITS * k);
   }
-  codes[(size_t)unit * n_quant * D * BITS / 8 + gid] = (uint8_t)v;
+  codes[((size_t)unit * cap32 + blk0) * block_bytes + gid] = (uint8_t)v;
 }
 
 __device__ __forceinline__ uint32_t unpack_code(const uint8_t* row, int d, int bits) {
@@ -160,44 +165,65 @@ __global__ void dequant_kernel(const uint8_t* __restrict__ codes, const H2* __re
 
 using namespace vc;
 
-extern "C" int vc_quantize_kv(const void* k_src, const void* v_src, int B, int Hkv, int L_cap, int D,
-                              const vc_kv_comp* out, hipStream_t stream) {
-  VC_CHECK(out != nullptr, "vc_quantize_kv: out descriptor is NULL");
-  VC_CHECK(out->kind == VC_KV_QUANT, "vc_quantize_kv: out->kind must be VC_KV_QUANT");
-  VC_CHECK(out->bits == 2 || out->bits == 4, "vc_quantize_kv: bits must be 2 or 4 (got %d)", out->bits);
-  VC_CHECK(B > 0 && Hkv > 0 && L_cap > 0, "vc_quantize_kv: bad B/Hkv/L_cap (%d,%d,%d)", B, Hkv, L_cap);
-  if (D != 64 && D != 128) return fail(VC_ERR_UNSUPPORTED, "vc_quantize_kv: D=%d not in {64,128}", D);
-  const int nq = out->n_quant;
-  VC_CHECK(nq >= 0 && nq % 32 == 0 && nq <= L_cap, "vc_quantize_kv: n_quant=%d must be a multiple of 32 <= L_cap", nq);
-  if (nq == 0) return VC_OK;
-  VC_CHECK(k_src && v_src && out->k_codes && out->v_codes && out->k_meta && out->v_meta,
-           "vc_quantize_kv: null pointer");
+// Quantise source rows [src_row0, src_row0 + 32 n_blocks) of every unit into
+// cache blocks [dst_block, dst_block + n_blocks) of out.
+static int quantize_blocks(const char* fn, const void* k_src, const void* v_src, int B, int Hkv, int src_cap, int D,
+                           int src_row0, int n_blocks, const vc_kv_comp* out, int dst_block, hipStream_t stream) {
+  VC_CHECK(out != nullptr, "%s: out descriptor is NULL", fn);
+  VC_CHECK(out->kind == VC_KV_QUANT, "%s: out->kind must be VC_KV_QUANT", fn);
+  VC_CHECK(out->bits == 2 || out->bits == 4, "%s: bits must be 2 or 4 (got %d)", fn, out->bits);
+  VC_CHECK(B > 0 && Hkv > 0 && src_cap > 0, "%s: bad B/Hkv/src rows (%d,%d,%d)", fn, B, Hkv, src_cap);
+  if (D != 64 && D != 128) return fail(VC_ERR_UNSUPPORTED, "%s: D=%d not in {64,128}", fn, D);
+  const int cap = quant_cap(out);
+  VC_CHECK(cap >= 0 && cap % 32 == 0, "%s: q_cap=%d must be a multiple of 32", fn, cap);
+  VC_CHECK(n_blocks >= 0 && src_row0 >= 0 && (long long)src_row0 + 32LL * n_blocks <= src_cap,
+           "%s: source rows [%d, %d) outside [0, %d)", fn, src_row0, src_row0 + 32 * n_blocks, src_cap);
+  VC_CHECK(dst_block >= 0 && 32LL * (dst_block + n_blocks) <= cap, "%s: blocks [%d, %d) outside the %d-row cache",
+           fn, dst_block, dst_block + n_blocks, cap);
+  if (n_blocks == 0) return VC_OK;
+  VC_CHECK(k_src && v_src && out->k_codes && out->v_codes && out->k_meta && out->v_meta, "%s: null pointer", fn);
   VC_CHECK(aligned(k_src, 2) && aligned(v_src, 2) && aligned(out->k_meta, 4) && aligned(out->v_meta, 4),
-           "vc_quantize_kv: misaligned pointer");
-  if (nq == 0) return VC_OK;
+           "%s: misaligned pointer", fn);
   const int units = B * Hkv;
   uint8_t* kc = const_cast<uint8_t*>(out->k_codes);
   uint8_t* vcodes = const_cast<uint8_t*>(out->v_codes);
   H2* km = reinterpret_cast<H2*>(const_cast<void*>(out->k_meta));
   H2* vm = reinterpret_cast<H2*>(const_cast<void*>(out->v_meta));
-  const uint16_t* ks = static_cast<const uint16_t*>(k_src);
-  const uint16_t* vs = static_cast<const uint16_t*>(v_src);
-  dim3 gk(nq / 32, units);
+  const uint16_t* ks = static_cast<const uint16_t*>(k_src) + (size_t)src_row0 * D;
+  const uint16_t* vs = static_cast<const uint16_t*>(v_src) + (size_t)src_row0 * D;
+  const int cap32 = cap / 32;
+  dim3 gk(n_blocks, units);
   const int cols = D * out->bits / 8;
   const int G = D / 32;
-  dim3 gv((nq * G + 255) / 256, units);
-  dim3 gp((nq / 32 * 4 * D * out->bits + 255) / 256, units);
+  dim3 gv((n_blocks * 32 * G + 255) / 256, units);
+  dim3 gp((n_blocks * 4 * D * out->bits + 255) / 256, units);
   if (out->bits == 4) {
-    quant_k_kernel<4><<<gk, cols, 0, stream>>>(ks, L_cap, D, nq, kc, km);
-    quant_v_meta_kernel<4><<<gv, 256, 0, stream>>>(vs, L_cap, D, nq, vm);
-    quant_v_pack_kernel<4><<<gp, 256, 0, stream>>>(vs, L_cap, D, nq, vm, vcodes);
+    quant_k_kernel<4><<<gk, cols, 0, stream>>>(ks, src_cap, D, dst_block, cap32, kc, km);
+    quant_v_meta_kernel<4><<<gv, 256, 0, stream>>>(vs, src_cap, D, n_blocks, dst_block, cap32, vm);
+    quant_v_pack_kernel<4><<<gp, 256, 0, stream>>>(vs, src_cap, D, n_blocks, dst_block, cap32, vm, vcodes);
   } else {
-    quant_k_kernel<2><<<gk, cols, 0, stream>>>(ks, L_cap, D, nq, kc, km);
-    quant_v_meta_kernel<2><<<gv, 256, 0, stream>>>(vs, L_cap, D, nq, vm);
-    quant_v_pack_kernel<2><<<gp, 256, 0, stream>>>(vs, L_cap, D, nq, vm, vcodes);
+    quant_k_kernel<2><<<gk, cols, 0, stream>>>(ks, src_cap, D, dst_block, cap32, kc, km);
+    quant_v_meta_kernel<2><<<gv, 256, 0, stream>>>(vs, src_cap, D, n_blocks, dst_block, cap32, vm);
+    quant_v_pack_kernel<2><<<gp, 256, 0, stream>>>(vs, src_cap, D, n_blocks, dst_block, cap32, vm, vcodes);
   }
   VC_HIP(hipGetLastError());
   return VC_OK;
+}
+
+extern "C" int vc_quantize_kv(const void* k_src, const void* v_src, int B, int Hkv, int L_cap, int D,
+                              const vc_kv_comp* out, hipStream_t stream) {
+  VC_CHECK(out != nullptr, "vc_quantize_kv: out descriptor is NULL");
+  const int nq = out->n_quant;
+  VC_CHECK(nq >= 0 && nq % 32 == 0 && nq <= L_cap, "vc_quantize_kv: n_quant=%d must be a multiple of 32 <= L_cap",
+           nq);
+  return quantize_blocks("vc_quantize_kv", k_src, v_src, B, Hkv, L_cap, D, 0, nq / 32, out, 0, stream);
+}
+
+extern "C" int vc_quantize_blocks(const void* k_src, const void* v_src, int B, int Hkv, int src_cap, int D,
+                                  int src_row0, int n_blocks, const vc_kv_comp* out, int dst_block,
+                                  hipStream_t stream) {
+  return quantize_blocks("vc_quantize_blocks", k_src, v_src, B, Hkv, src_cap, D, src_row0, n_blocks, out,
+                         dst_block, stream);
 }
 
 extern "C" int vc_debug_dequant(const vc_kv_comp* comp, int B, int Hkv, int D, int b, int h, int which,
@@ -210,11 +236,13 @@ extern "C" int vc_debug_dequant(const vc_kv_comp* comp, int B, int Hkv, int D, i
   const int nq = comp->n_quant;
   VC_CHECK(nq >= 0 && nq % 32 == 0, "vc_debug_dequant: bad n_quant");
   if (nq == 0) return VC_OK;
+  const int cap = quant_cap(comp);
+  VC_CHECK(cap >= nq && cap % 32 == 0, "vc_debug_dequant: q_cap=%d below n_quant=%d or not a multiple of 32", cap, nq);
   const size_t unit = (size_t)b * Hkv + h;
   const int row_bytes = D * comp->bits / 8;
-  const uint8_t* codes = (which == 0 ? comp->k_codes : comp->v_codes) + unit * nq * row_bytes;
+  const uint8_t* codes = (which == 0 ? comp->k_codes : comp->v_codes) + unit * cap * row_bytes;
   const H2* meta = reinterpret_cast<const H2*>(which == 0 ? comp->k_meta : comp->v_meta);
-  meta += unit * (nq / 32) * D;  // both: D dwords per 32-token block
+  meta += unit * (cap / 32) * D;  // both: D dwords per 32-token block
   VC_CHECK(codes && meta, "vc_debug_dequant: null codes/meta");
   const int n = nq * D;
   dequant_kernel<<<(n + 255) / 256, 256, 0, stream>>>(codes, meta, comp->bits, nq, D, which, out);

@@ -30,6 +30,9 @@ int num_cus();  // compute units of the current device (cached per device)
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Rows per (batch, kv-head) the code and metadata arrays of a QUANT cache hold.
+inline int quant_cap(const vc_kv_comp* c) { return c->q_cap > 0 ? c->q_cap : c->n_quant; }
+
 // ---------------------------------------------------------- device utils ---
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;

@@ -51,11 +51,12 @@ extern "C" {
 #define VC_KV_TOKEN_DROP 2 /* a kept subset of context rows, by index      */
 
 /*
- * QUANT layout (per (b, kv-head) slices are dense and consecutive):
- *   k_codes  u8 [B][Hkv][n_quant][D*bits/8]  codes of token t packed along D:
+ * QUANT layout (per (b, kv-head) slices are consecutive; each holds Q = q_cap
+ * rows, q_cap = n_quant when the field is 0, of which [0, n_quant) are live):
+ *   k_codes  u8 [B][Hkv][Q][D*bits/8]  codes of token t packed along D:
  *            4-bit: channel 2i in the low nibble of byte i, 2i+1 in the high
  *            nibble; 2-bit: channel i at bit 2*(i%4) of byte i/4.
- *   v_codes  u8 [B][Hkv][n_quant/32][32*D*bits/8]  tiled: the codes of each
+ *   v_codes  u8 [B][Hkv][Q/32][32*D*bits/8]  tiled: the codes of each
  *            block of 32 tokens are laid out as the operands of the draft
  *            kernel's matrix product.  Token tau (0..31) of a block, channel c:
  *              q = (tau % 16) / 4, e = tau % 4 + 4 * (tau / 16),
@@ -64,7 +65,7 @@ extern "C" {
  *              bit = bits * j + 16 * hf,
  *              byte = lane * (D*bits/16) + 4 * dword + bit / 8,
  *            code at bit (bit % 8) of that byte.  vc_quantize_kv writes it.
- *   k_meta   f16 [B][Hkv][n_quant/32][2][D]  per 32-token block, a plane of
+ *   k_meta   f16 [B][Hkv][Q/32][2][D]  per 32-token block, a plane of
  *            the scales and then a plane of the zeros of the groups formed by
  *            the block's 32 tokens of one channel, each plane in pair order:
  *            channel c (quad = c / (D/4), r = c % (D/4), cpd = 32/bits,
@@ -73,7 +74,7 @@ extern "C" {
  *              2 * ((quad * (D/32) + pi / 4) * 4 + pi % 4) + h,
  *            so that each dword pairs the two channels one K code dword holds
  *            at bits b and b + 16.
- *   v_meta   f16x2 [B][Hkv][n_quant/32][D/32][32]  {scale, zero} of the group
+ *   v_meta   f16x2 [B][Hkv][Q/32][D/32][32]  {scale, zero} of the group
  *            formed by 32 consecutive channels of one token; token tau of a
  *            block sits in slot 8 * ((tau % 16) / 4) + tau % 4 + 4 * (tau / 16).
  *   All four arrays must be 16-byte aligned for vc_draft_attn.
@@ -99,6 +100,9 @@ typedef struct vc_kv_comp {
   int L_cap;         /* IDENTITY/TOKEN_DROP: row capacity of k_full */
   const int32_t* keep_idx;
   int n_keep;        /* TOKEN_DROP: kept rows per (b, kv-head)      */
+  int q_cap;         /* QUANT: rows each (b, kv-head) slice of the code
+                        and meta arrays holds, % 32 == 0, >= n_quant;
+                        0 means n_quant (a cache that never grows)  */
 } vc_kv_comp;
 
 /*
@@ -147,11 +151,34 @@ const char* vc_last_error(void);
  * Per group: mn/mx exact; s = f16((mx - mn) / (2^bits - 1)) and z = f16(mn)
  * (fp32 subtract and divide, round-to-nearest-even); code = 0 if s == 0, else
  * clamp(rint((x - z) / s), 0, 2^bits - 1) in fp32.  Writes the QUANT layout
- * above (out->k_codes etc. are written through; kind/bits/n_quant are read).
- * D in {64, 128}; bits in {2, 4}; n_quant % 32 == 0, n_quant <= L_cap.
+ * above (out->k_codes etc. are written through; kind/bits/n_quant/q_cap are
+ * read).  D in {64, 128}; bits in {2, 4}; n_quant % 32 == 0, n_quant <= L_cap,
+ * n_quant <= q_cap.
  */
 int vc_quantize_kv(const void* k_src, const void* v_src, int B, int Hkv, int L_cap, int D,
                    const vc_kv_comp* out, hipStream_t stream);
+
+/*
+ * vc_quantize_blocks — grow a QUANT cache by whole 32-token blocks: the rows
+ * that leave the exact recent window are quantised into the next blocks of
+ * the cache.  [VC Architecture Support: KIVI keeps a full-precision recent
+ * window and quantises tokens that leave it; VC Problem Statement: the
+ * compressed cache is kept up to date as decoding proceeds]
+ * Source rows [src_row0, src_row0 + 32 * n_blocks) of every (b, kv-head) of
+ * k_src / v_src (device bf16 [B][Hkv][src_rows][D]) become cache blocks
+ * [dst_block, dst_block + n_blocks) of out, with the same per-group
+ * arithmetic as vc_quantize_kv, so that quantising a context in pieces gives
+ * the same bytes as quantising it at once.  Needs
+ * 32 * (dst_block + n_blocks) <= q_cap (out->q_cap must be set, or n_quant
+ * large enough).  out->n_quant is neither read nor changed: the caller
+ * raises it (in its own descriptor) once the blocks are written, by
+ * 32 * n_blocks when they are appended.  n_blocks == 0 is a no-op.
+ * Errors: VC_ERR_INVALID for a range outside the source or the cache, a bad
+ * kind/bits or a null pointer; VC_ERR_UNSUPPORTED for D not in {64, 128}.
+ * Launches on `stream`; nothing is allocated.
+ */
+int vc_quantize_blocks(const void* k_src, const void* v_src, int B, int Hkv, int src_rows, int D, int src_row0,
+                       int n_blocks, const vc_kv_comp* out, int dst_block, hipStream_t stream);
 
 /*
  * vc_select_top_m — the token-dropping compressor's selection: for each of
@@ -166,8 +193,9 @@ int vc_quantize_kv(const void* k_src, const void* v_src, int B, int Hkv, int L_c
 int vc_select_top_m(const float* scores, int rows, int L, int M, int32_t* keep_idx, hipStream_t stream);
 
 /*
- * vc_debug_dequant — dequantised K (which = 0) or V (which = 1) of one
- * (b, kv-head) as fp32 [n_quant][D] into out (device).  For bit-exact checks.
+ * vc_debug_dequant — dequantised K (which = 0) or V (which = 1) of the live
+ * rows [0, n_quant) of one (b, kv-head) as fp32 [n_quant][D] into out
+ * (device).  For bit-exact checks.
  */
 int vc_debug_dequant(const vc_kv_comp* comp, int B, int Hkv, int D, int b, int h, int which,
                      float* out, hipStream_t stream);

@@ -74,6 +74,29 @@ def test_host_validation_without_gpu(lib):
     m = lib.vc_verify_merge
     m.restype = ctypes.c_int
     assert m(None, 0, 8, 64, 33, 128, None, None) == -1
+    # rollover quantiser: descriptor checks and range checks against the source
+    # and the cache capacity all come before any launch
+    qb = lib.vc_quantize_blocks
+    qb.restype = ctypes.c_int
+    assert qb(None, None, 1, 1, 64, 128, 0, 1, None, 0, None) == -1
+
+    class Desc(ctypes.Structure):
+        _fields_ = [("kind", ctypes.c_int), ("bits", ctypes.c_int), ("n_quant", ctypes.c_int)] + \
+                   [(f, ctypes.c_void_p) for f in ("k_codes", "v_codes", "k_meta", "v_meta", "k_full", "v_full")] + \
+                   [("L_full", ctypes.c_int), ("L_cap", ctypes.c_int), ("keep_idx", ctypes.c_void_p),
+                    ("n_keep", ctypes.c_int), ("q_cap", ctypes.c_int)]
+    d = Desc(kind=1, bits=2, n_quant=64, q_cap=128)
+    ref = ctypes.byref(d)
+    assert qb(None, None, 1, 1, 256, 128, 0, 0, ref, 4, None) == 0            # empty append at the end
+    assert qb(None, None, 1, 1, 256, 128, 0, 1, ref, 4, None) == -1           # past the capacity
+    assert b"outside" in lib.vc_last_error()
+    assert qb(None, None, 1, 1, 256, 128, 240, 1, ref, 2, None) == -1         # past the source rows
+    assert qb(None, None, 1, 1, 256, 128, 0, 1, ref, 2, None) == -1           # null sources
+    assert qb(None, None, 1, 1, 256, 96, 0, 1, ref, 2, None) == -2           # D=96 unsupported
+    d.q_cap = 100
+    assert qb(None, None, 1, 1, 256, 128, 0, 1, ref, 0, None) == -1           # capacity not a multiple of 32
+    d.kind = 2
+    assert qb(None, None, 1, 1, 256, 128, 0, 1, ref, 0, None) == -1
 
 
 def test_no_oracle_in_product_path():

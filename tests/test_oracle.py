@@ -122,6 +122,31 @@ def test_quant_k_v_grouping_axes():
     assert float(vs.sum()) == float(vs[7, 1])
 
 
+def test_quant_blocks_are_independent():
+    """What makes a rolled-over cache equal a one-shot one: every group, and
+    every packed byte and metadata word, depends on the rows of its own
+    32-token block only, so the cache of rows [0, n) is the concatenation of the
+    caches of its blocks."""
+    rng = np.random.default_rng(7)
+    n, D, bits = 128, 64, 2
+    k = (rng.standard_normal((n, D)) * rng.uniform(0.1, 4, (n, 1))).astype(np.float32)
+    v = (rng.standard_normal((n, D)) * rng.uniform(0.1, 4, (1, D))).astype(np.float32)
+    c, s, z = O.quantize_k(k, bits)
+    cv, sv, zv = O.quantize_v(v, bits)
+    kb = [O.quantize_k(k[i:i + 32], bits) for i in range(0, n, 32)]
+    vb = [O.quantize_v(v[i:i + 32], bits) for i in range(0, n, 32)]
+    assert np.array_equal(O.pack_codes(c, bits), np.concatenate([O.pack_codes(b[0], bits) for b in kb]))
+    assert np.array_equal(O.pack_k_meta(s, z, bits), np.concatenate([O.pack_k_meta(b[1], b[2], bits) for b in kb]))
+    assert np.array_equal(O.pack_v_codes_tiled(cv, bits),
+                          np.concatenate([O.pack_v_codes_tiled(b[0], bits) for b in vb]))
+    assert np.array_equal(O.pack_v_meta(sv, zv), np.concatenate([O.pack_v_meta(b[1], b[2]) for b in vb]))
+    # and a block's K groups do see all of its 32 rows: changing one row moves them
+    k2 = k.copy()
+    k2[40] += 100.0
+    assert not np.array_equal(O.quantize_k(k2, bits)[1][1], s[1])
+    assert np.array_equal(O.quantize_k(k2, bits)[1][0], s[0])
+
+
 def test_pack_codes_bit_layout():
     c4 = np.array([[1, 2, 3, 4, 15, 0, 9, 10]], np.uint8)
     assert list(O.pack_codes(c4, 4)[0]) == [0x21, 0x43, 0x0F, 0xA9]

@@ -113,6 +113,79 @@ def test_quantize_bit_exact(D, bits):
             assert np.array_equal(dq.astype(np.float64), O.dequant_v(c, s, z)), (b, h, "v dequant")
 
 
+ROLLOVER_CASES = [(64, 4), (128, 2), (128, 4)]
+
+
+@pytest.mark.parametrize("D,bits", ROLLOVER_CASES)
+def test_quantize_rollover_blocks(D, bits):
+    """A QUANT cache grown block by block (rows leaving the exact window are
+    quantised into the next blocks of a larger-capacity cache) holds the bytes
+    the oracle's one-shot quantisation of the whole prefix gives, leaves the
+    rows past n_quant untouched, and drafts over the capacity stride correctly."""
+    import torch
+    vc = _vc()
+    from compressed_kv_draft_amd.workload import bf16_dev
+    print(f"[case] rollover D={D} bits={bits}", flush=True)
+    w = C.TINY.with_(B=2, Hkv=2, Hq=8, D=D, L=448, seed=61 + D + bits)
+    K = I.context_kv(w, "k")
+    V = I.context_kv(w, "v")
+    n0, cap, R = 96, 384, 40
+    comp = vc.quantize_kv(bf16_dev(K, "cuda"), bf16_dev(V, "cuda"), bits, n0, capacity=cap)
+    for f in ("k_codes", "v_codes", "k_meta", "v_meta"):  # sentinel past the live rows
+        t = comp.t[f].view(torch.uint8).view(w.B, w.Hkv, -1)
+        t[:, :, t.shape[2] * n0 // cap:] = 0xA5
+    # the exact window lives in its own buffer: rows [off, off + m) of it are
+    # context rows [n, n + m); appends read it at a row offset
+    off = 8
+    win_k = np.zeros((w.B, w.Hkv, off + w.L - n0, D), dtype=np.uint16)
+    win_v = np.zeros_like(win_k)
+    win_k[:, :, off:] = K[:, :, n0:]
+    win_v[:, :, off:] = V[:, :, n0:]
+    wk, wv = bf16_dev(win_k, "cuda"), bf16_dev(win_v, "cuda")
+    n = n0
+    for nb in (3, 1, 4):
+        vc.quantize_blocks(wk, wv, comp, off + n - n0, nb)
+        n += 32 * nb
+    assert n == comp.t["n_quant"] == comp.desc.n_quant == 352
+    torch.cuda.synchronize()
+    kc = comp.t["k_codes"].cpu().numpy()
+    vcd = comp.t["v_codes"].cpu().numpy()
+    km = comp.t["k_meta"].cpu().numpy()
+    vm = comp.t["v_meta"].cpu().numpy()
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            kf = O.bf16_to_f64(K[b, h, :n]).astype(np.float32)
+            vf = O.bf16_to_f64(V[b, h, :n]).astype(np.float32)
+            c, s, z = O.quantize_k(kf, bits)
+            assert np.array_equal(kc[b, h, :n], O.pack_codes(c, bits)), (b, h, "k codes")
+            assert np.array_equal(km[b, h, :n // 32].view(np.uint16), O.pack_k_meta(s, z, bits)), (b, h, "k meta")
+            dq = vc.debug_dequant(comp, w.B, w.Hkv, D, b, h, 0).cpu().numpy()
+            assert np.array_equal(dq.astype(np.float64), O.dequant_k(c, s, z)), (b, h, "k dequant")
+            c, s, z = O.quantize_v(vf, bits)
+            assert np.array_equal(vcd[b, h, :n].reshape(-1), O.pack_v_codes_tiled(c, bits)), (b, h, "v codes")
+            assert np.array_equal(vm[b, h, :n // 32].view(np.uint16), O.pack_v_meta(s, z)), (b, h, "v meta")
+            for arr, nb_rows in ((kc, n), (vcd, n), (km, n // 32), (vm, n // 32)):
+                assert (arr[b, h, nb_rows:].view(np.uint8) == 0xA5).all(), (b, h, "past n_quant")
+    # draft over the grown cache: quantised [0, n), then exact rows [n, n + R)
+    tk = bf16_dev(np.ascontiguousarray(K[:, :, n:n + R]), "cuda")
+    tv = bf16_dev(np.ascontiguousarray(V[:, :, n:n + R]), "cuda")
+    tail = vc.Tail(tk, tv, torch.full((w.B,), R, dtype=torch.int32, device="cuda"))
+    Q = I.queries(w)[:, :, 0]
+    scale = O.scale_for(D)
+    got = vc.draft_attn(comp, tail, bf16_dev(np.ascontiguousarray(Q), "cuda"), scale).cpu().numpy()
+    g = w.Hq // w.Hkv
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            kf = O.bf16_to_f64(K[b, h, :n]).astype(np.float32)
+            vf = O.bf16_to_f64(V[b, h, :n]).astype(np.float32)
+            keys, vals = O.draft_kv_rows("quant", k_deq=O.dequant_k(*O.quantize_k(kf, bits)),
+                                         v_deq=O.dequant_v(*O.quantize_v(vf, bits)),
+                                         tail_k=O.bf16_to_f64(K[b, h, n:n + R]),
+                                         tail_v=O.bf16_to_f64(V[b, h, n:n + R]))
+            ref = O.draft_attention_unit(O.bf16_to_f64(Q[b, h * g:(h + 1) * g]), keys, vals, scale)
+            assert_close(got[b, h * g:(h + 1) * g], ref, f"rollover draft D{D} int{bits} b{b} h{h}")
+
+
 VERIFY_CASES = [
     C.TINY,
     C.TINY.with_(name="v_d128_g4_k32", B=2, Hq=8, Hkv=2, D=128, L=1000, k=32, seed=41),
