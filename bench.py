@@ -41,6 +41,9 @@ def parse():
     p.add_argument("--e2e", action="store_true",
                    help="end-to-end draft-then-verify generation with the tiny decoder (256 tokens, int4 draft, "
                         "k = 32): verified tokens/s and the acceptance histogram instead of the per-layer line")
+    p.add_argument("--e2e-groups", action="store_true",
+                   help="two request groups of the tiny decoder: lock-step vs staggered on two streams, fixed vs "
+                        "adaptive draft length (vc_sched_choose_k); prints that JSON line instead")
     p.add_argument("--stagger", action="store_true",
                    help="measure the full-KV prefetch of one request group against the other group's drafting "
                         "(Llama-70B-shaped paged workload) and print that JSON line instead")
@@ -394,6 +397,65 @@ def e2e(a):
     print(json.dumps(line), flush=True)
 
 
+def e2e_groups(a):
+    """Two request groups of the tiny decoder (prompts 0 and 1, 256 tokens
+    each), decode only: lock-step on one stream with k = 32, staggered on two
+    streams with k = 32, and staggered with the draft length chosen per round
+    by vc_sched_choose_k from each group's acceptance history and event-timed
+    phases.  Reports summed tokens/s, the draft lengths used, and whether every
+    run emitted the same tokens (group 0 also against the stored oracle
+    sequence)."""
+    import numpy as np
+    import torch
+
+    from compressed_kv_draft_amd.groups import StaggeredGroups
+    from compressed_kv_draft_amd.tinylm import TinyLM
+    from synth import configs as C
+    from synth import model as M
+    cfg = C.LM_E2E
+    W = M.weights(cfg)
+    cos, sin = M.rope_tables(cfg)
+    prompts = [M.prompt(cfg, r) for r in (0, 1)]
+    gold = None
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tests", "golden", f"e2e_{cfg.name}.txt")
+    if os.path.exists(path):
+        for line in open(path):
+            if line.startswith("tokens="):
+                gold = [int(x) for x in line.split("=", 1)[1].split()]
+    modes = {"lockstep_k32": (False, cfg.k, cfg.k), "staggered_k32": (True, cfg.k, cfg.k),
+             "staggered_adaptive": (True, 1, cfg.k)}
+    out, toks_ref = {}, None
+    same = True
+    for name, (stag, kmin, kmax) in modes.items():
+        best = None
+        for i in range(a.warmup_e2e + a.steps_e2e):
+            base = TinyLM(cfg, W, cos, sin)
+            lms = [base, TinyLM(cfg, None, None, None, shared=base)]
+            res = StaggeredGroups(lms, k_min=kmin, k_max=kmax, stagger=stag).run(prompts, cfg.n_gen)
+            toks = [[int(x) for x in t] for t in res["tokens"]]
+            toks_ref = toks if toks_ref is None else toks_ref
+            same = same and toks == toks_ref
+            if i >= a.warmup_e2e and (best is None or res["wall_s"] < best["wall_s"]):
+                best = res
+            del lms, base
+            torch.cuda.empty_cache()
+        out[name] = {"tokens_per_s": round(best["tokens_per_s"], 1), "decode_s": round(best["wall_s"], 4),
+                     "rounds": [len(r) for r in best["rounds"]],
+                     "k_per_round": [[r["k"] for r in g] for g in best["rounds"]],
+                     "mean_tokens_per_round": [round(float(np.mean([r["n"] + 1 for r in g])), 2)
+                                               for g in best["rounds"]]}
+        print(f"[e2e-groups] {name}: {out[name]['tokens_per_s']} tokens/s", flush=True)
+    line = {"metric": "end-to-end verified tokens/s, two request groups (tiny decoder, greedy)",
+            "value": out["staggered_adaptive"]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+            "steps": a.steps_e2e, "warmup": a.warmup_e2e, "higher_is_better": True, "data": "synthetic",
+            "config": {"workload": cfg.name + "_x2_groups", "groups": 2, "prompt": cfg.prompt,
+                       "generated_per_group": cfg.n_gen, "k_max": cfg.k,
+                       "dense_layers": "torch fp32 (outside the measured path)"},
+            "modes": out, "all_runs_same_tokens": same,
+            "group0_equals_oracle_greedy": (toks_ref[0] == gold) if gold is not None else None}
+    print(json.dumps(line), flush=True)
+
+
 def full_kv_decode(w, dw, value, step_s, launches=20):
     """Baseline without drafting: one decode step reads the whole bf16 cache
     (vc_draft_attn with the identity compressor over the L context rows plus the
@@ -441,6 +503,9 @@ def main():
         return
     if a.e2e:
         e2e(a)
+        return
+    if a.e2e_groups:
+        e2e_groups(a)
         return
     import numpy as np
     import torch

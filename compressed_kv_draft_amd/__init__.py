@@ -8,5 +8,5 @@ from ._lib import (  # noqa: F401
     select_top_m,
     debug_dequant, draft_ws_bytes, draft_attn, verify_ws_bytes, verify_attn, verify_range_parts,
     verify_attn_range, verify_merge, argmax, accept,
-    prefetch_full_kv,
+    prefetch_full_kv, sched_accept_rate, sched_expected_tokens, sched_choose_k,
 )

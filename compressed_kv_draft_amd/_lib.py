@@ -46,6 +46,10 @@ EXPORTS = {
     "vc_quantize_blocks": (c_int, [c_void, c_void, c_int, c_int, c_int, c_int, c_int, c_int,
                                    ctypes.POINTER(VcKvComp), c_int, c_void]),
     "vc_select_top_m": (c_int, [c_void, c_int, c_int, c_int, c_void, c_void]),
+    "vc_sched_accept_rate": (ctypes.c_double, [ctypes.c_longlong, ctypes.c_longlong]),
+    "vc_sched_expected_tokens": (ctypes.c_double, [ctypes.c_double, c_int]),
+    "vc_sched_choose_k": (c_int, [ctypes.c_longlong, ctypes.c_longlong, ctypes.c_double, ctypes.c_double,
+                                  ctypes.c_double, c_int, c_int]),
     "vc_debug_dequant": (c_int, [ctypes.POINTER(VcKvComp), c_int, c_int, c_int, c_int, c_int, c_int, c_void, c_void]),
     "vc_draft_ws_bytes": (c_size, [c_int, c_int, c_int, c_int, c_int]),
     "vc_draft_attn": (c_int, [ctypes.POINTER(VcKvComp), ctypes.POINTER(VcTail), c_void, c_void, c_void,
@@ -213,6 +217,23 @@ def select_top_m(scores: torch.Tensor, M: int, keep_idx=None, stream=None) -> to
         keep_idx = torch.empty((*scores.shape[:-1], M), dtype=torch.int32, device=scores.device)
     _check(LIB.vc_select_top_m(_ptr(scores), rows, L, int(M), _ptr(keep_idx), _stream(stream)), "vc_select_top_m")
     return keep_idx
+
+
+def sched_accept_rate(accepted: int, rejections: int) -> float:
+    return float(LIB.vc_sched_accept_rate(int(accepted), int(rejections)))
+
+
+def sched_expected_tokens(a: float, k: int) -> float:
+    return float(LIB.vc_sched_expected_tokens(float(a), int(k)))
+
+
+def sched_choose_k(accepted: int, rejections: int, t_draft: float, t_overlap: float, t_rest: float, k_min: int,
+                   k_max: int) -> int:
+    """Draft length of a group's next round (host policy; see include/vc.h)."""
+    k = LIB.vc_sched_choose_k(int(accepted), int(rejections), float(t_draft), float(t_overlap), float(t_rest),
+                              int(k_min), int(k_max))
+    _check(k if k < 0 else 0, "vc_sched_choose_k")
+    return int(k)
 
 
 def draft_ws_bytes(B, Hq, Hkv, D, max_keys) -> int:

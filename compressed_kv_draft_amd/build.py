@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvc.so")
-SOURCES = ["vc_core.cpp", "quant.hip", "select.hip", "draft.hip", "verify.hip", "accept.hip", "prefetch.cpp"]
+SOURCES = ["vc_core.cpp", "quant.hip", "select.hip", "draft.hip", "verify.hip", "accept.hip", "prefetch.cpp", "sched.cpp"]
 ARCH = os.environ.get("VC_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -39,18 +39,26 @@ def _bf16_to_f32(bits: np.ndarray, device) -> torch.Tensor:
 
 
 class TinyLM:
-    def __init__(self, cfg, W: dict, cos: np.ndarray, sin: np.ndarray, device="cuda"):
+    def __init__(self, cfg, W: dict | None, cos: np.ndarray | None, sin: np.ndarray | None, device="cuda",
+                 shared: "TinyLM | None" = None):
+        """shared: another instance whose weights and rotary tables this one
+        reuses (a second request group of the same model); W, cos, sin are
+        then ignored.  Every instance has its own caches."""
         torch.backends.cuda.matmul.allow_tf32 = False
         self.cfg, self.dev = cfg, device
         c = cfg
-        f = lambda b: _bf16_to_f32(b, device)  # noqa: E731
-        self.embed = f(W["embed"])
-        self.layers = [{n: f(W[n][l]) for n in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down",
-                                                   "attn_norm", "ffn_norm")} for l in range(c.n_layers)]
-        self.final_norm = f(W["final_norm"])
-        self.head = f(W["lm_head"])
-        self.cos = torch.from_numpy(np.ascontiguousarray(cos)).to(device)
-        self.sin = torch.from_numpy(np.ascontiguousarray(sin)).to(device)
+        if shared is not None:
+            for n in ("embed", "layers", "final_norm", "head", "cos", "sin"):
+                setattr(self, n, getattr(shared, n))
+        else:
+            f = lambda b: _bf16_to_f32(b, device)  # noqa: E731
+            self.embed = f(W["embed"])
+            self.layers = [{n: f(W[n][l]) for n in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down",
+                                                       "attn_norm", "ffn_norm")} for l in range(c.n_layers)]
+            self.final_norm = f(W["final_norm"])
+            self.head = f(W["lm_head"])
+            self.cos = torch.from_numpy(np.ascontiguousarray(cos)).to(device)
+            self.sin = torch.from_numpy(np.ascontiguousarray(sin)).to(device)
         self.scale = float(np.float32(1.0 / np.sqrt(c.D)))
         bf = dict(dtype=torch.bfloat16, device=device)
         self.K = [torch.zeros((1, c.Hkv, c.L_cap, c.D), **bf) for _ in range(c.n_layers)]
@@ -202,6 +210,68 @@ class TinyLM:
 
     # ------------------------------------------------------------ the loop
 
+    def start(self, prompt: np.ndarray, graph: bool = False):
+        """Prefill, the first token and (graph) the recorded draft position, on
+        the current stream.  Then draft_round / verify_round advance the loop."""
+        c = self.cfg
+        self.P = len(prompt)
+        ids = torch.from_numpy(np.asarray(prompt, dtype=np.int32)).to(self.dev)
+        lg = self.prefill(ids)
+        self.pending = vc.argmax(lg[None])                  # int32 [1]
+        self.use_graph = graph
+        if graph:
+            self._capture_draft_step()
+        self.out = [int(self.pending.item())]
+        self.top1 = [float(lg.max().item())]
+        self.ctx = self.P
+        self.accepted = []
+        self.drafts = torch.empty((1, c.k), dtype=torch.int32, device=self.dev)
+
+    def done(self, n_gen: int) -> bool:
+        return len(self.out) >= n_gen
+
+    def draft_round(self, k: int):
+        """Enqueue k draft positions (k <= cfg.k) on the current stream."""
+        c = self.cfg
+        if not 1 <= k <= c.k:
+            raise ValueError(f"draft length {k} outside [1, {c.k}]")
+        ctx, P = self.ctx, self.P
+        if self.use_graph:
+            self.g_tok.copy_(self.pending)
+            self.g_pos.fill_(ctx)
+            self.g_row.fill_(ctx - P)
+            self.g_j.zero_()
+            for _ in range(k):
+                self.graph.replay()
+            self.drafts[0, :k].copy_(self.g_drafts[:k])
+        else:
+            tok = self.pending
+            for j in range(k):
+                lgd = self.draft_step(tok, ctx + j, ctx - P + j)
+                tok = vc.argmax(lgd, ids=self.drafts[0, j:j + 1])
+
+    def verify_round(self, k: int) -> int:
+        """Verify the pending token and the k drafts of the last draft_round in
+        one causal pass, accept, and move the verified rows into the draft
+        tail.  Waits for the accept result; returns the accepted count."""
+        c = self.cfg
+        ctx, P = self.ctx, self.P
+        seq = torch.cat([self.pending, self.drafts[0, :k]])
+        x = self.causal_pass(seq, ctx)
+        vlog = self._logits(x)
+        emitted, n_acc = vc.accept(self.drafts[:, :k].contiguous(), vlog[None])
+        n = int(n_acc.item())
+        self.out.extend(emitted[0, :n + 1].tolist())
+        self.top1.extend(vlog[:n + 1].max(dim=-1).values.tolist())
+        self.accepted.append(n)
+        r0 = ctx - P
+        for l in range(c.n_layers):
+            self.TK[l][0, :, r0:r0 + n + 1] = self.K[l][0, :, ctx:ctx + n + 1]
+            self.TV[l][0, :, r0:r0 + n + 1] = self.V[l][0, :, ctx:ctx + n + 1]
+        self.ctx = ctx + n + 1
+        self.pending = emitted[0, n:n + 1].clone()
+        return n
+
     def generate(self, prompt: np.ndarray, n_gen: int, graph: bool = False):
         """Returns (tokens [n_gen] list, per-round accepted counts, stats dict
         with timings and the logit of every emitted token).  graph: replay a
@@ -209,55 +279,22 @@ class TinyLM:
         its ~200 launches from the host each time (recorded after the
         prefill, outside the timed decode)."""
         c = self.cfg
-        P = len(prompt)
-        ids = torch.from_numpy(np.asarray(prompt, dtype=np.int32)).to(self.dev)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        lg = self.prefill(ids)
-        pending = vc.argmax(lg[None])                       # int32 [1]
+        self.start(prompt, graph=False)
         torch.cuda.synchronize()
         t_pre = time.perf_counter()
         if graph:
+            self.use_graph = True
             self._capture_draft_step()
             torch.cuda.synchronize()
         t1 = time.perf_counter()
-        out = [int(pending.item())]
-        top1 = [float(lg.max().item())]
-        ctx = P
-        accepted = []
-        drafts = torch.empty((1, c.k), dtype=torch.int32, device=self.dev)
-        while len(out) < n_gen:
-            if graph:
-                self.g_tok.copy_(pending)
-                self.g_pos.fill_(ctx)
-                self.g_row.fill_(ctx - P)
-                self.g_j.zero_()
-                for j in range(c.k):
-                    self.graph.replay()
-                drafts[0].copy_(self.g_drafts)
-            else:
-                tok = pending
-                for j in range(c.k):
-                    lgd = self.draft_step(tok, ctx + j, ctx - P + j)
-                    tok = vc.argmax(lgd, ids=drafts[0, j:j + 1])
-            seq = torch.cat([pending, drafts[0]])
-            x = self.causal_pass(seq, ctx)
-            vlog = self._logits(x)
-            emitted, n_acc = vc.accept(drafts, vlog[None])
-            n = int(n_acc.item())
-            em = emitted[0, :n + 1].tolist()
-            out.extend(em)
-            top1.extend(vlog[:n + 1].max(dim=-1).values.tolist())
-            accepted.append(n)
-            r0 = ctx - P
-            for l in range(c.n_layers):
-                self.TK[l][0, :, r0:r0 + n + 1] = self.K[l][0, :, ctx:ctx + n + 1]
-                self.TV[l][0, :, r0:r0 + n + 1] = self.V[l][0, :, ctx:ctx + n + 1]
-            ctx += n + 1
-            pending = emitted[0, n:n + 1].clone()
+        while not self.done(n_gen):
+            self.draft_round(c.k)
+            self.verify_round(c.k)
         torch.cuda.synchronize()
         t2 = time.perf_counter()
-        out = out[:n_gen]
-        stats = dict(prefill_s=t_pre - t0, decode_s=t2 - t1, rounds=len(accepted), top1=top1[:n_gen], graph=graph,
-                     tokens_per_s=(len(out) - 1) / (t2 - t1) if t2 > t1 else 0.0)
-        return out, accepted, stats
+        out = self.out[:n_gen]
+        stats = dict(prefill_s=t_pre - t0, decode_s=t2 - t1, rounds=len(self.accepted), top1=self.top1[:n_gen],
+                     graph=graph, tokens_per_s=(len(out) - 1) / (t2 - t1) if t2 > t1 else 0.0)
+        return out, self.accepted, stats

@@ -330,6 +330,51 @@ int vc_prefetch_full_kv(const void* host_pool, size_t page_bytes, int n_slots, c
                         int tok_begin, int tok_end, int page_tokens, void* staging, size_t staging_bytes,
                         void* dev_dst, hipEvent_t staging_free, hipStream_t copy_stream, hipEvent_t done);
 
+/* ------------------------------------------------------------------------ */
+/* Staggering scheduler policy (host only: no device work, no GPU needed)    */
+/* [VC Key System Innovations P2: long drafts amortise verification when     */
+/*  acceptance is high; P1: one group drafts while another loads its full KV */
+/*  and verifies]  The pages state the principle; the rule below is this     */
+/* library's.                                                                */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * vc_sched_accept_rate — per-draft match probability estimated from a
+ * group's history: `accepted` = drafts accepted over its rounds (the sum of
+ * n_accept), `rejections` = rounds that stopped at a mismatch (n_accept < k).
+ * Returns (accepted + 1) / (accepted + rejections + 2) (the estimate with one
+ * prior match and one prior mismatch, so it lies in (0, 1)); NaN for negative
+ * counts.
+ */
+double vc_sched_accept_rate(long long accepted, long long rejections);
+
+/*
+ * vc_sched_expected_tokens — tokens a round with draft length k emits on
+ * average when each draft matches with probability a until the first
+ * mismatch: the accepted drafts plus the verifier's token,
+ * 1 + a + a^2 + ... + a^k, summed in that order in fp64.  NaN for a outside
+ * [0, 1] or k < 0.
+ */
+double vc_sched_expected_tokens(double a, int k);
+
+/*
+ * vc_sched_choose_k — draft length of a group's next round: the k in
+ * [k_min, k_max] that maximises
+ *   vc_sched_expected_tokens(a, k) / (max(k * t_draft, t_overlap) + t_rest),
+ * a = vc_sched_accept_rate(accepted, rejections), ties to the smaller k.
+ *   t_draft    time of one draft step of this group
+ *   t_overlap  work of the other group that this group's drafting runs
+ *              beside (its full-KV transfer and verification); 0 unstaggered
+ *   t_rest     the rest of the cycle, independent of k (this group's own
+ *              verification and accept, or the other group's drafting when
+ *              that is longer)
+ * Any time unit, the same for all three.  Returns k >= 1, or VC_ERR_INVALID
+ * for negative counts, 1 <= k_min <= k_max <= 64 violated, t_draft <= 0, or a
+ * negative or non-finite time.
+ */
+int vc_sched_choose_k(long long accepted, long long rejections, double t_draft, double t_overlap, double t_rest,
+                      int k_min, int k_max);
+
 #ifdef __cplusplus
 }
 #endif

@@ -67,8 +67,10 @@ def weights(cfg: TinyLM) -> dict:
     return W
 
 
-def prompt(cfg: TinyLM) -> np.ndarray:
-    return rng(cfg.seed, "prompt").integers(0, cfg.vocab, size=cfg.prompt).astype(np.int64)
+def prompt(cfg: TinyLM, request: int = 0) -> np.ndarray:
+    """Prompt ids of request `request` (request 0 is the configuration's own prompt)."""
+    g = rng(cfg.seed, "prompt") if request == 0 else rng(cfg.seed, "prompt", request)
+    return g.integers(0, cfg.vocab, size=cfg.prompt).astype(np.int64)
 
 
 def rope_tables(cfg: TinyLM, n_pos: int | None = None):

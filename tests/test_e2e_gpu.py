@@ -95,3 +95,47 @@ def test_e2e_small_lm_equals_oracle_greedy():
         _compare(cfg, toks, acc, stats, [int(x) for x in want], list(top), list(marg))
         runs[graph] = (toks, acc)
     assert runs[True] == runs[False]
+
+
+def test_staggered_groups_adaptive_k_equal_oracle_greedy():
+    """Two request groups on two streams (one verifies while the other
+    drafts), each choosing its draft length per round with the library's
+    policy, emit the oracle's greedy tokens for their prompts; so does the
+    lock-step order on one stream.  With a fixed clock the decisions are
+    reproducible and each equals the oracle's rule on the inputs the scheduler
+    passed, whose acceptance counts must be the running sums of the rounds'
+    outcomes.  One group's clock makes drafting dear, so it runs short rounds
+    (draft lengths below the maximum take the variable-length path)."""
+    from compressed_kv_draft_amd.groups import StaggeredGroups
+    from compressed_kv_draft_amd.tinylm import TinyLM
+    from oracle import e2e as E
+    from oracle import sched as S
+    cfg = C.LM_SMALL
+    W = M.weights(cfg)
+    cos, sin = M.rope_tables(cfg)
+    m = E.Model(cfg, W, cos, sin)
+    prompts = [M.prompt(cfg, r) for r in (0, 1)]
+    want = [[int(x) for x in E.greedy_decode(m, p, cfg.n_gen)[0]] for p in prompts]
+    fixed = {0: (0.1, 0.5), 1: (1.0, 0.5)}
+    for stagger, clock in ((True, fixed.get), (True, None), (False, fixed.get)):
+        print(f"[case] groups stagger={stagger} clock={'fixed' if clock else 'events'}", flush=True)
+        base = TinyLM(cfg, W, cos, sin)
+        lms = [base, TinyLM(cfg, None, None, None, shared=base)]
+        res = StaggeredGroups(lms, k_min=1, k_max=cfg.k, stagger=stagger, clock=clock).run(prompts, cfg.n_gen)
+        for g in range(2):
+            ks = [r["k"] for r in res["rounds"][g]]
+            print(f"  group {g}: k per round {ks}, accepted {[r['n'] for r in res['rounds'][g]]}", flush=True)
+            assert [int(x) for x in res["tokens"][g]] == want[g], (stagger, g)
+            acc = rej = 0
+            for i, r in enumerate(res["rounds"][g]):
+                assert 0 <= r["n"] <= r["k"] <= cfg.k
+                acc += r["n"]
+                rej += r["n"] < r["k"]
+                if "next_k" in r:
+                    a = r["policy_args"]
+                    assert (a[0], a[1]) == (acc, rej)
+                    assert r["next_k"] == S.choose_k(*a)
+                    assert res["rounds"][g][i + 1]["k"] == r["next_k"]
+        if clock is not None:
+            assert min(r["k"] for r in res["rounds"][1]) < cfg.k
+        del lms, base
