@@ -602,3 +602,58 @@ def test_prefetched_pages_feed_paged_verify():
         for h in range(w.Hkv):
             ref = R.unit_verify(w, K[b, h], V[b, h], Kn[b, h], Vn[b, h], Q[b, h * g:(h + 1) * g])
             assert_close(got[b, h * g:(h + 1) * g], ref, f"prefetched paged verify b{b} h{h}")
+
+
+def test_round_graph_replays_match_eager():
+    """The round as the benchmark launches it, each phase (the k draft calls,
+    verify, accept) recorded once as a HIP graph, gives bit-identical outputs
+    to the eager calls on every replay, with eager work, scrambled outputs and
+    synchronisation between the replays (nothing recorded may depend on state
+    that only the first replay sees)."""
+    import torch
+    vc = _vc()
+    from compressed_kv_draft_amd.workload import DeviceWorkload
+    w = C.TINY.with_(name="graph_int2_d128_g4", B=2, Hq=8, Hkv=2, D=128, L=1056, k=5, bits=2, residual=32,
+                     seed=71)
+    print(f"[case] graph replay {w.name}", flush=True)
+    dw = DeviceWorkload(w)
+    for j in range(w.k):
+        dw.draft_step(j)
+    d_ids = vc.argmax(dw.draft_logits().contiguous()).reshape(w.B, w.k)
+    dw.verify()
+    vlog = dw.verify_logits()
+    out_ids = torch.empty((w.B, w.n_q), dtype=torch.int32, device="cuda")
+    n_acc = torch.empty(w.B, dtype=torch.int32, device="cuda")
+
+    def drafts():
+        for j in range(w.k):
+            dw.draft_step(j)
+
+    def accept():
+        vc.accept(d_ids, vlog, out_ids=out_ids, n_accept=n_acc)
+
+    phases = [drafts, dw.verify, accept]
+    for ph in phases:
+        ph()
+    torch.cuda.synchronize()
+    outs = [dw.draft_out, dw.verify_out, out_ids, n_acc]
+    ref = [t.clone() for t in outs]
+    graphs = []
+    for ph in phases:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            ph()
+        graphs.append(g)
+    bits = lambda t: t.view(torch.int32) if t.dtype == torch.float32 else t  # noqa: E731
+    for r in range(4):
+        dw.draft_out.fill_(float("nan"))
+        dw.verify_out.fill_(-1.0)
+        out_ids.fill_(-7)
+        n_acc.fill_(-7)
+        dw.draft_step(1)          # eager work between replays
+        torch.cuda.synchronize()
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("draft", "verify", "ids", "n_accept"), outs, ref):
+            assert torch.equal(bits(got), bits(want)), (r, name)
