@@ -71,6 +71,20 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 w) {
   return r;
 }
 
+// The XOR key of key row `row` in the LDS tile layout: 16-byte chunk c of the
+// row sits at chunk position c ^ swz(row).  Chosen so that both operand reads
+// hit distinct banks: a K read (16 consecutive rows, one chunk each) needs
+// distinct keys per 256-byte bank window, a transposed V read (8 consecutive
+// rows, an aligned chunk pair each) distinct keys >> 1.  With 256-byte rows
+// (D = 128) rotating the row's low 4 bits left by one does both (row % 16
+// alone maps rows r and r ^ 1 onto the same chunk pair); with 128-byte rows
+// (D = 64, two rows per window) rows of one parity must differ.
+template <int CPR>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (CPR == 16) return ((row << 1) | ((row >> 3) & 1)) & 15;
+  else return ((row >> 1) & 3) << 1 | ((row >> 3) & 1);
+}
+
 template <int D, int MT, bool PAGED, int NW>
 __global__ __launch_bounds__(64 * NW) void verify_mfma_kernel(VerifyArgs a) {
   constexpr int NKS = D / 32, NCT = D / 16;
@@ -145,7 +159,7 @@ __global__ __launch_bounds__(64 * NW) void verify_mfma_kernel(VerifyArgs a) {
   // global->LDS loads issued kDepth - 1 tiles ahead; no registers hold them in flight.
   // In round r a thread of staging wavefront wave < LW fills LDS chunk
   // s = (r * LW + wave) * 64 + lane
-  // of the tile, which holds 16-byte chunk (s % CPR) ^ (key % CPR) of key row
+  // of the tile, which holds 16-byte chunk (s % CPR) ^ swz(key) of key row
   // key = s / CPR: the XOR swizzle makes the operand reads below conflict-free.
   // The rows of one load instruction lie in one page (pages hold >= 8 rows).
   const uint32_t lds0 = lds_address(smem);
@@ -165,7 +179,7 @@ __global__ __launch_bounds__(64 * NW) void verify_mfma_kernel(VerifyArgs a) {
 #pragma unroll
     for (int r = 0; r < ROUNDS; ++r) {
       const int s = (r * LW + wave) * 64 + lane;
-      const int row = s / CPR, cc = (s % CPR) ^ (row % CPR);
+      const int row = s / CPR, cc = (s % CPR) ^ swz<CPR>(row);
       // rows past the split's range are clamped to its last row (masked later)
       const int key = min(t0 + row, ke - 1);
       const unsigned char *kp, *vp;
@@ -263,7 +277,7 @@ __global__ __launch_bounds__(64 * NW) void verify_mfma_kernel(VerifyArgs a) {
       // each read issued one step ahead of its use
       auto kread = [&](int idx) __attribute__((always_inline)) {
         const int row = 16 * (idx / NKS) + col, c = quad * (CPR / 4) + idx % NKS;
-        return *reinterpret_cast<const bf16x8*>(kt + (row * CPR + (c ^ (row % CPR))) * 16);
+        return *reinterpret_cast<const bf16x8*>(kt + (row * CPR + (c ^ swz<CPR>(row))) * 16);
       };
       f32x4 s[LIVE > 0 ? LIVE : 1][2];
 #pragma unroll
@@ -335,9 +349,9 @@ __global__ __launch_bounds__(64 * NW) void verify_mfma_kernel(VerifyArgs a) {
         const int c = 2 * ct + ((col & 3) >> 1);
         const int r0 = 4 * quad + (col >> 2), r1 = r0 + 16;
         const uint16_t* p0 =
-            reinterpret_cast<const uint16_t*>(vt + (r0 * CPR + (c ^ (r0 % CPR))) * 16 + 8 * (col & 1));
+            reinterpret_cast<const uint16_t*>(vt + (r0 * CPR + (c ^ swz<CPR>(r0))) * 16 + 8 * (col & 1));
         const uint16_t* p1 =
-            reinterpret_cast<const uint16_t*>(vt + (r1 * CPR + (c ^ (r1 % CPR))) * 16 + 8 * (col & 1));
+            reinterpret_cast<const uint16_t*>(vt + (r1 * CPR + (c ^ swz<CPR>(r1))) * 16 + 8 * (col & 1));
         const s16x4 lo4 = lds_read_tr16(p0);
         const s16x4 hi4 = lds_read_tr16(p1);
         return __builtin_bit_cast(f16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
