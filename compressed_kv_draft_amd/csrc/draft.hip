@@ -63,6 +63,7 @@ struct DraftArgs {
   int tail_first, tail_bpw;   // workgroups >= tail_first first take tail_bpw exact tail blocks
   int splits;                 // partials per (batch, kv-head): main_splits + tail workgroups
   int direct;                 // 1: a single partial, written as the output
+  int xcd_affine;             // 1: 1-D grid, every split of unit u on XCD u % 8 (units % 8 == 0)
   float* ws;                  // split partials [splits][B][Hq][D + 2]
 };
 
@@ -340,9 +341,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
   constexpr int NKS = C::NKS, NCT = C::NCT, NG = C::NG;
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM];
 
-  const int unit = blockIdx.y;
+  // Workgroups are dispatched to the 8 XCDs round-robin by id.  With an
+  // XCD-affine grid, the splits of one (batch, kv-head) unit all run on one
+  // XCD, so the partials they write stay in that XCD's L2 for the combine.
+  int unit, split;
+  if (a.xcd_affine) {
+    const int id = blockIdx.x, x8 = id % 8, y = id / 8;
+    unit = (y / a.main_splits) * 8 + x8;
+    split = y % a.main_splits;
+  } else {
+    unit = blockIdx.y;
+    split = blockIdx.x;
+  }
   const int b = unit / a.Hkv, hk = unit % a.Hkv;
-  const int split = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, quad = lane >> 4;
   const int g = a.g;
@@ -693,11 +704,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
 // so that up to kCombineChunk splits cost one memory latency and one barrier.
 constexpr int kCombineChunk = 16;
 constexpr int kMaxCombineSplits = 256;
+// g_affine > 0: the rows of unit u (g_affine query heads each) are merged on
+// XCD u % 8, where the draft kernel's XCD-affine grid wrote their partials.
 __global__ __launch_bounds__(128) void draft_combine_kernel(const float* __restrict__ ws, int splits, int rows,
                                                             int D, float* __restrict__ out,
-                                                            float* __restrict__ lse) {
+                                                            float* __restrict__ lse, int g_affine) {
   __shared__ float s_m[kMaxCombineSplits], s_l[kMaxCombineSplits];
-  const int row = blockIdx.x, d = threadIdx.x;
+  int row = blockIdx.x;
+  if (g_affine > 0) {
+    const int x8 = row % 8, y = row / 8;
+    row = ((y / g_affine) * 8 + x8) * g_affine + y % g_affine;
+  }
+  const int d = threadIdx.x;
   float o[kCombineChunk];
 #pragma unroll
   for (int j = 0; j < kCombineChunk; ++j)
@@ -915,11 +933,16 @@ extern "C" int vc_draft_attn(const vc_kv_comp* comp, const vc_tail* tail, const 
   a.tail_bpw = p.tail_bpw;
   a.splits = p.splits;
   a.direct = p.splits == 1;
-  dim3 grid(p.main_splits, units);
-  kern<<<grid, kThreads, 0, stream>>>(a);
+  a.xcd_affine = units % 8 == 0 ? 1 : 0;
+  if (a.xcd_affine) {
+    VC_CHECK((long long)p.main_splits * units < (1LL << 31), "vc_draft_attn: grid too large");
+    kern<<<dim3(p.main_splits * units), kThreads, 0, stream>>>(a);
+  } else {
+    kern<<<dim3(p.main_splits, units), kThreads, 0, stream>>>(a);
+  }
   VC_HIP(hipGetLastError());
   if (p.splits > 1) {
-    draft_combine_kernel<<<B * Hq, D, 0, stream>>>(a.ws, p.splits, B * Hq, D, out, lse);
+    draft_combine_kernel<<<B * Hq, D, 0, stream>>>(a.ws, p.splits, B * Hq, D, out, lse, a.xcd_affine ? g : 0);
     VC_HIP(hipGetLastError());
   }
   return VC_OK;
