@@ -51,6 +51,14 @@ DRAFT_CASES = [
     C.TINY.with_(name="int4_d64_allresidual", B=1, Hq=8, Hkv=2, D=64, L=96, k=3, bits=4, residual=96, seed=29),
     C.TINY.with_(name="int2_d128_g4_splits", B=1, Hq=4, Hkv=1, D=128, L=16512, k=2, bits=2, residual=128,
                  seed=30),
+    # (batch x kv-head) units a multiple of 8: the XCD-affine grid and combine row mapping
+    C.TINY.with_(name="xcd_int2_d128_g4_u8", B=2, Hq=16, Hkv=4, D=128, L=2080, k=3, bits=2, residual=64, seed=32),
+    C.TINY.with_(name="xcd_int4_d64_g2_u16", B=4, Hq=8, Hkv=4, D=64, L=1100, k=2, bits=4, residual=44, seed=33),
+    C.TINY.with_(name="xcd_drop_d128_g8_u8", B=1, Hq=64, Hkv=8, D=128, L=3000, k=2, kind="token_drop",
+                 keep_frac=0.2, seed=34),
+    C.TINY.with_(name="xcd_identity_d128_g1_u8", B=8, Hq=8, Hkv=8, D=128, L=500, k=2, kind="identity", seed=35),
+    C.TINY.with_(name="xcd_int2_d128_g4_u8_ragged", B=2, Hq=16, Hkv=4, D=128, L=70, k=2, bits=2, residual=38,
+                 seed=36),
 ]
 
 
