@@ -406,14 +406,16 @@ def e2e_groups(a):
     each), decode only: lock-step on one stream with k = 32, staggered on two
     streams with k = 32, and staggered with the draft length chosen per round
     by vc_sched_choose_k from each group's acceptance history and event-timed
-    phases.  Reports summed tokens/s, the draft lengths used, and whether every
+    phases; then lock-step and staggered-adaptive again with the full caches
+    in pinned host memory, copied into one shared device region before each
+    verification (the copy beside the other group's drafting when staggered).  Reports summed tokens/s, the draft lengths used, and whether every
     run emitted the same tokens (group 0 also against the stored oracle
     sequence)."""
     import numpy as np
     import torch
 
     from compressed_kv_draft_amd.groups import StaggeredGroups
-    from compressed_kv_draft_amd.tinylm import TinyLM
+    from compressed_kv_draft_amd.tinylm import FullStaging, TinyLM
     from synth import configs as C
     from synth import model as M
     cfg = C.LM_E2E
@@ -426,22 +428,25 @@ def e2e_groups(a):
         for line in open(path):
             if line.startswith("tokens="):
                 gold = [int(x) for x in line.split("=", 1)[1].split()]
-    modes = {"lockstep_k32": (False, cfg.k, cfg.k), "staggered_k32": (True, cfg.k, cfg.k),
-             "staggered_adaptive": (True, 1, cfg.k)}
+    modes = {"lockstep_k32": (False, cfg.k, cfg.k, False), "staggered_k32": (True, cfg.k, cfg.k, False),
+             "staggered_adaptive": (True, 1, cfg.k, False),
+             "lockstep_k32_host_full_kv": (False, cfg.k, cfg.k, True),
+             "staggered_adaptive_host_full_kv": (True, 1, cfg.k, True)}
     out, toks_ref = {}, None
     same = True
-    for name, (stag, kmin, kmax) in modes.items():
+    for name, (stag, kmin, kmax, host) in modes.items():
         best = None
         for i in range(a.warmup_e2e + a.steps_e2e):
-            base = TinyLM(cfg, W, cos, sin)
-            lms = [base, TinyLM(cfg, None, None, None, shared=base)]
+            st = FullStaging(cfg) if host else None
+            base = TinyLM(cfg, W, cos, sin, staging=st)
+            lms = [base, TinyLM(cfg, None, None, None, shared=base, staging=st)]
             res = StaggeredGroups(lms, k_min=kmin, k_max=kmax, stagger=stag).run(prompts, cfg.n_gen)
             toks = [[int(x) for x in t] for t in res["tokens"]]
             toks_ref = toks if toks_ref is None else toks_ref
             same = same and toks == toks_ref
             if i >= a.warmup_e2e and (best is None or res["wall_s"] < best["wall_s"]):
                 best = res
-            del lms, base
+            del lms, base, st
             torch.cuda.empty_cache()
         out[name] = {"tokens_per_s": round(best["tokens_per_s"], 1), "decode_s": round(best["wall_s"], 4),
                      "rounds": [len(r) for r in best["rounds"]],

@@ -15,6 +15,12 @@ runs beside drafting of the next: with two groups the phases alternate
 all groups share one stream, so the same calls run one after another (the
 lock-step order).
 
+Groups built with a shared FullStaging keep their full caches in pinned host
+memory.  The next group's full cache is then copied into the staging region on
+a copy stream as soon as the current group's verification has released it, so
+the transfer runs beside the drafting.  This is the single-GPU form of P1:
+drafting streams HBM while the other group's full KV crosses PCIe.
+
 The policy sees, per group, the accepted drafts and the rounds that ended at a
 mismatch and the mean time of one draft step and of one verification so far
 (HIP events on the group's stream, or a fixed clock for reproducible
@@ -49,8 +55,12 @@ class StaggeredGroups:
         G = len(self.lms)
         if self.stagger:
             streams = [torch.cuda.Stream() for _ in range(G)]
+            copy_stream = torch.cuda.Stream()
         else:
             streams = [torch.cuda.current_stream()] * G
+            copy_stream = streams[0]
+        host_kv = self.lms[0].staging is not None
+        fetched = [False] * G
         for lm, p, s in zip(self.lms, prompts, streams):
             with torch.cuda.stream(s):
                 lm.start(p, graph=graph)
@@ -80,11 +90,22 @@ class StaggeredGroups:
                 if not active[g]:
                     continue
                 lm = self.lms[g]
+                if host_kv and not fetched[g]:
+                    lm.fetch(copy_stream)
                 with torch.cuda.stream(streams[g]):
                     v0, v1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     v0.record()
                     n = lm.verify_round(ks[g])
                     v1.record()
+                fetched[g] = False
+                if host_kv:   # the next verifying group's full cache, beside this group's drafting
+                    for d in range(1, G):
+                        h = (g + d) % G
+                        if active[h]:
+                            if not fetched[h]:
+                                self.lms[h].fetch(copy_stream)
+                                fetched[h] = True
+                            break
                 v1.synchronize()
                 k = ks[g]
                 rec = dict(k=k, n=n)

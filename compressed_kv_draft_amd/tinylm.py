@@ -34,16 +34,35 @@ import torch.nn.functional as F
 from . import _lib as vc
 
 
+class FullStaging:
+    """One device region for the full cache of whichever request group is
+    verifying: bf16 [1, Hkv, L_cap, D] K and V per layer.  [VC Key System
+    Innovations P1; Architecture Support: full KV kept in CPU memory]  Groups
+    that share it keep their own full caches in pinned host memory, copy them
+    in before each verification (TinyLM.fetch) and write the rows it adds back
+    out; `free` marks the end of the last use."""
+
+    def __init__(self, cfg, device="cuda"):
+        bf = dict(dtype=torch.bfloat16, device=device)
+        self.K = [torch.zeros((1, cfg.Hkv, cfg.L_cap, cfg.D), **bf) for _ in range(cfg.n_layers)]
+        self.V = [torch.zeros((1, cfg.Hkv, cfg.L_cap, cfg.D), **bf) for _ in range(cfg.n_layers)]
+        self.full = [vc.FullKV(self.K[l], self.V[l], L_cap=cfg.L_cap) for l in range(cfg.n_layers)]
+        self.free = torch.cuda.Event()
+
+
 def _bf16_to_f32(bits: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16).float()
 
 
 class TinyLM:
     def __init__(self, cfg, W: dict | None, cos: np.ndarray | None, sin: np.ndarray | None, device="cuda",
-                 shared: "TinyLM | None" = None):
+                 shared: "TinyLM | None" = None, staging: FullStaging | None = None):
         """shared: another instance whose weights and rotary tables this one
         reuses (a second request group of the same model); W, cos, sin are
-        then ignored.  Every instance has its own caches."""
+        then ignored.  Every instance has its own draft caches.  staging: keep
+        the full cache in pinned host memory and verify in this shared device
+        region (fetch() before each verification); None keeps it on the
+        device."""
         torch.backends.cuda.matmul.allow_tf32 = False
         self.cfg, self.dev = cfg, device
         c = cfg
@@ -61,9 +80,17 @@ class TinyLM:
             self.sin = torch.from_numpy(np.ascontiguousarray(sin)).to(device)
         self.scale = float(np.float32(1.0 / np.sqrt(c.D)))
         bf = dict(dtype=torch.bfloat16, device=device)
-        self.K = [torch.zeros((1, c.Hkv, c.L_cap, c.D), **bf) for _ in range(c.n_layers)]
-        self.V = [torch.zeros((1, c.Hkv, c.L_cap, c.D), **bf) for _ in range(c.n_layers)]
-        self.full = [vc.FullKV(self.K[l], self.V[l], L_cap=c.L_cap) for l in range(c.n_layers)]
+        self.staging = staging
+        if staging is not None:
+            self.K, self.V, self.full = staging.K, staging.V, staging.full
+            pin = dict(dtype=torch.bfloat16, pin_memory=True)
+            self.K_h = [torch.zeros((1, c.Hkv, c.L_cap, c.D), **pin) for _ in range(c.n_layers)]
+            self.V_h = [torch.zeros((1, c.Hkv, c.L_cap, c.D), **pin) for _ in range(c.n_layers)]
+            self.landed = torch.cuda.Event()
+        else:
+            self.K = [torch.zeros((1, c.Hkv, c.L_cap, c.D), **bf) for _ in range(c.n_layers)]
+            self.V = [torch.zeros((1, c.Hkv, c.L_cap, c.D), **bf) for _ in range(c.n_layers)]
+            self.full = [vc.FullKV(self.K[l], self.V[l], L_cap=c.L_cap) for l in range(c.n_layers)]
         self.TK = [torch.zeros((1, c.Hkv, c.T_cap, c.D), **bf) for _ in range(c.n_layers)]
         self.TV = [torch.zeros((1, c.Hkv, c.T_cap, c.D), **bf) for _ in range(c.n_layers)]
         self.tail_len = torch.zeros(1, dtype=torch.int32, device=device)
@@ -136,8 +163,12 @@ class TinyLM:
         the last prompt position's logits [V]."""
         c = self.cfg
         P = prompt.shape[0]
+        if self.staging is not None:
+            torch.cuda.current_stream().wait_event(self.staging.free)
         x = self.causal_pass(prompt, 0)
         self.comp = [vc.quantize_kv(self.K[l], self.V[l], c.bits, P) for l in range(c.n_layers)]
+        if self.staging is not None:
+            self._write_back(0, P)
         self.draft_ws = torch.zeros(vc.draft_ws_bytes(1, c.Hq, c.Hkv, c.D, P + c.T_cap), dtype=torch.uint8,
                                     device=self.dev)
         return self._logits(x[-1:])[0]
@@ -157,6 +188,27 @@ class TinyLM:
                               ws=self.draft_ws, Hkv=c.Hkv)
             x = self._finish(l, x, o[0][:, None, :])
         return self._logits(x)
+
+    # ------------------------------------------------------------ host-resident full cache
+
+    def _write_back(self, r0: int, n: int):
+        """Rows [r0, r0 + n) of the staging region -> this group's host cache,
+        then mark the region free (on the current stream)."""
+        for l in range(self.cfg.n_layers):
+            self.K_h[l][0, :, r0:r0 + n].copy_(self.K[l][0, :, r0:r0 + n], non_blocking=True)
+            self.V_h[l][0, :, r0:r0 + n].copy_(self.V[l][0, :, r0:r0 + n], non_blocking=True)
+        self.staging.free.record(torch.cuda.current_stream())
+
+    def fetch(self, copy_stream):
+        """Copy this group's full cache into the staging region on copy_stream,
+        once the region's last user is done with it; verify_round waits for
+        the copy."""
+        copy_stream.wait_event(self.staging.free)
+        with torch.cuda.stream(copy_stream):
+            for l in range(self.cfg.n_layers):
+                self.K[l].copy_(self.K_h[l], non_blocking=True)
+                self.V[l].copy_(self.V_h[l], non_blocking=True)
+            self.landed.record(copy_stream)
 
     def _pos(self, pos: int) -> torch.Tensor:
         return torch.full((1,), pos, dtype=torch.int64, device=self.dev)
@@ -256,6 +308,8 @@ class TinyLM:
         tail.  Waits for the accept result; returns the accepted count."""
         c = self.cfg
         ctx, P = self.ctx, self.P
+        if self.staging is not None:
+            torch.cuda.current_stream().wait_event(self.landed)
         seq = torch.cat([self.pending, self.drafts[0, :k]])
         x = self.causal_pass(seq, ctx)
         vlog = self._logits(x)
@@ -268,6 +322,8 @@ class TinyLM:
         for l in range(c.n_layers):
             self.TK[l][0, :, r0:r0 + n + 1] = self.K[l][0, :, ctx:ctx + n + 1]
             self.TV[l][0, :, r0:r0 + n + 1] = self.V[l][0, :, ctx:ctx + n + 1]
+        if self.staging is not None:
+            self._write_back(ctx, n + 1)
         self.ctx = ctx + n + 1
         self.pending = emitted[0, n:n + 1].clone()
         return n

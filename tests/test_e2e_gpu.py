@@ -139,3 +139,29 @@ def test_staggered_groups_adaptive_k_equal_oracle_greedy():
         if clock is not None:
             assert min(r["k"] for r in res["rounds"][1]) < cfg.k
         del lms, base
+
+
+def test_staggered_groups_host_full_kv_equal_oracle_greedy():
+    """Full caches in pinned host memory and one shared device staging region
+    (each group's full KV is copied in before its verification while the
+    other group drafts, and the rows it adds are written back): both groups
+    still emit the oracle's greedy tokens, staggered and lock-step."""
+    from compressed_kv_draft_amd.groups import StaggeredGroups
+    from compressed_kv_draft_amd.tinylm import FullStaging, TinyLM
+    from oracle import e2e as E
+    cfg = C.LM_SMALL
+    W = M.weights(cfg)
+    cos, sin = M.rope_tables(cfg)
+    m = E.Model(cfg, W, cos, sin)
+    prompts = [M.prompt(cfg, r) for r in (0, 1)]
+    want = [[int(x) for x in E.greedy_decode(m, p, cfg.n_gen)[0]] for p in prompts]
+    for stagger, clock in ((True, None), (False, {0: (1.0, 6.0), 1: (1.0, 0.5)}.get)):
+        print(f"[case] groups host full KV stagger={stagger}", flush=True)
+        st = FullStaging(cfg)
+        base = TinyLM(cfg, W, cos, sin, staging=st)
+        lms = [base, TinyLM(cfg, None, None, None, shared=base, staging=st)]
+        res = StaggeredGroups(lms, k_min=1, k_max=cfg.k, stagger=stagger, clock=clock).run(prompts, cfg.n_gen)
+        for g in range(2):
+            print(f"  group {g}: k per round {[r['k'] for r in res['rounds'][g]]}", flush=True)
+            assert [int(x) for x in res["tokens"][g]] == want[g], (stagger, g)
+        del lms, base, st
