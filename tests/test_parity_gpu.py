@@ -665,3 +665,53 @@ def test_round_graph_replays_match_eager():
         torch.cuda.synchronize()
         for name, got, want in zip(("draft", "verify", "ids", "n_accept"), outs, ref):
             assert torch.equal(bits(got), bits(want)), (r, name)
+
+
+def _random_cases(n=14, seed=2026):
+    """Seeded draws over the parameters the kernels branch on: cache kind and
+    bits, head dim, GQA group, unit count (so both grid mappings), context
+    length (ragged against 32-token blocks and tiles), draft length and
+    exact-window length."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        kind = ["quant2", "quant4", "token_drop", "identity"][i % 4]
+        D = int(rng.choice([64, 128]))
+        g = int(rng.choice([1, 2, 4, 8]))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        B = int(rng.integers(1, 5))
+        L = int(rng.integers(40, 2600))
+        k = int(rng.integers(1, 7))
+        kw = dict(name=f"rand{i}_{kind}_d{D}_g{g}_b{B}x{Hkv}_l{L}_k{k}", B=B, Hq=g * Hkv, Hkv=Hkv, D=D, L=L, k=k,
+                  seed=100 + i)
+        if kind.startswith("quant"):
+            R = L % 32 + 32 * int(rng.integers(0, 4))
+            R = min(R, L)
+            kw.update(kind="quant", bits=int(kind[-1]), residual=R)
+        elif kind == "token_drop":
+            kw.update(kind="token_drop", keep_frac=float(rng.uniform(0.05, 0.6)))
+        else:
+            kw.update(kind="identity")
+        out.append(C.TINY.with_(**kw))
+    return out
+
+
+@pytest.mark.parametrize("w", _random_cases(), ids=lambda w: w.name)
+def test_random_shapes_draft_and_verify(w):
+    from compressed_kv_draft_amd.workload import DeviceWorkload
+    print(f"[case] random {w.name}", flush=True)
+    dw = DeviceWorkload(w, with_vocab=False)
+    for j in range(w.k):
+        dw.draft_step(j)
+    got_d = dw.draft_out.cpu().numpy()
+    got_v = dw.verify().cpu().numpy()
+    g = w.g
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            keep = dw.keep_np[b, h] if w.kind == "token_drop" else None
+            args = (dw.np["K"][b, h], dw.np["V"][b, h], dw.np["Kn"][b, h], dw.np["Vn"][b, h],
+                    dw.np["Q"][b, h * g:(h + 1) * g])
+            ref_d = R.unit_draft(w, *args, keep=keep)
+            assert_close(got_d[:, b, h * g:(h + 1) * g].transpose(1, 0, 2), ref_d, f"{w.name} draft b{b} h{h}")
+            ref_v = R.unit_verify(w, *args)
+            assert_close(got_v[b, h * g:(h + 1) * g], ref_v, f"{w.name} verify b{b} h{h}")
