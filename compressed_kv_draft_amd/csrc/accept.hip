@@ -9,7 +9,8 @@
 namespace vc {
 namespace {
 
-constexpr int kArgThreads = 256;
+constexpr int kArgThreads = 1024;
+constexpr int kArgLoads = 8;  // 16-byte loads in flight per thread
 
 // (value, index) max with ties to the lower index; NaN never wins a compare.
 __device__ __forceinline__ void better(float& v, int& i, float v2, int i2) {
@@ -25,14 +26,26 @@ __global__ __launch_bounds__(kArgThreads) void argmax_kernel(const float* __rest
   const float* p = x + (size_t)row * V;
   float bv = kNegInf;
   int bi = 0x7fffffff;
-  if ((V & 3) == 0) {
+  if ((V & 3) == 0 && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+    // 16-byte loads, kArgLoads of them in flight per thread before any compare
+    // (the running best is order-independent: ties go to the lowest index)
     const float4* p4 = reinterpret_cast<const float4*>(p);
-    for (int i = threadIdx.x; i < V / 4; i += kArgThreads) {
-      const float4 w = p4[i];
-      better(bv, bi, w.x, 4 * i);
-      better(bv, bi, w.y, 4 * i + 1);
-      better(bv, bi, w.z, 4 * i + 2);
-      better(bv, bi, w.w, 4 * i + 3);
+    const int n4 = V / 4;
+    for (int i = threadIdx.x; i < n4; i += kArgLoads * kArgThreads) {
+      float4 w[kArgLoads];
+#pragma unroll
+      for (int u = 0; u < kArgLoads; ++u) {
+        const int j = i + u * kArgThreads;
+        w[u] = j < n4 ? p4[j] : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+      }
+#pragma unroll
+      for (int u = 0; u < kArgLoads; ++u) {
+        const int j = 4 * (i + u * kArgThreads);
+        better(bv, bi, w[u].x, j);
+        better(bv, bi, w[u].y, j + 1);
+        better(bv, bi, w[u].z, j + 2);
+        better(bv, bi, w[u].w, j + 3);
+      }
     }
   } else {
     for (int i = threadIdx.x; i < V; i += kArgThreads) better(bv, bi, p[i], i);
