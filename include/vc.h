@@ -189,6 +189,9 @@ int vc_quantize_blocks(const void* k_src, const void* v_src, int B, int Hkv, int
  * equals +0); NaN scores give an unspecified (but valid, sorted, unique) set.
  * 0 <= M <= L.  [VC Problem Statement: token dropping; VC Architecture
  * Support: token-dropping compressors behind the uniform interface]
+ * Errors: VC_ERR_INVALID for rows < 0, L < 0, M outside [0, L], or a NULL
+ * scores / keep_idx when there is work; rows == 0 or M == 0 is a no-op.
+ * One workgroup per row on `stream`; nothing is allocated.
  */
 int vc_select_top_m(const float* scores, int rows, int L, int M, int32_t* keep_idx, hipStream_t stream);
 
