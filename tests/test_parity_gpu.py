@@ -715,3 +715,39 @@ def test_random_shapes_draft_and_verify(w):
             assert_close(got_d[:, b, h * g:(h + 1) * g].transpose(1, 0, 2), ref_d, f"{w.name} draft b{b} h{h}")
             ref_v = R.unit_verify(w, *args)
             assert_close(got_v[b, h * g:(h + 1) * g], ref_v, f"{w.name} verify b{b} h{h}")
+
+
+def test_select_then_token_drop_draft():
+    """The token-dropping compressor end to end on the GPU: importance scores
+    -> vc_select_top_m -> a VC_KV_TOKEN_DROP cache -> vc_draft_attn, against
+    the oracle's selection and its attention over the kept rows plus the tail.
+    Ragged L and M, and scores with ties at the selection boundary."""
+    import torch
+    vc = _vc()
+    from compressed_kv_draft_amd.workload import bf16_dev
+    from synth.gen import f32_to_bf16_bits
+    print("[case] select -> token-drop draft", flush=True)
+    rng = np.random.default_rng(77)
+    B, Hq, Hkv, D, L, M, T = 2, 16, 4, 128, 1517, 301, 9
+    k = f32_to_bf16_bits(rng.standard_normal((B, Hkv, L, D)).astype(np.float32))
+    v = f32_to_bf16_bits(rng.standard_normal((B, Hkv, L, D)).astype(np.float32))
+    tk = f32_to_bf16_bits(rng.standard_normal((B, Hkv, T, D)).astype(np.float32))
+    tv = f32_to_bf16_bits(rng.standard_normal((B, Hkv, T, D)).astype(np.float32))
+    q = f32_to_bf16_bits(rng.standard_normal((B, Hq, D)).astype(np.float32))
+    scores = rng.integers(0, 40, size=(B, Hkv, L)).astype(np.float32) / 8.0   # many ties
+    keep = vc.select_top_m(torch.from_numpy(scores).cuda(), M)
+    comp = vc.token_drop_cache(bf16_dev(k, "cuda"), bf16_dev(v, "cuda"), keep)
+    tail = vc.Tail(bf16_dev(tk, "cuda"), bf16_dev(tv, "cuda"), torch.full((B,), T, dtype=torch.int32, device="cuda"))
+    scale = O.scale_for(D)
+    got = vc.draft_attn(comp, tail, bf16_dev(q, "cuda"), scale).cpu().numpy()
+    keep_np = keep.cpu().numpy()
+    g = Hq // Hkv
+    for b in range(B):
+        for h in range(Hkv):
+            want_idx = O.select_top_m(scores[b, h], M)
+            assert np.array_equal(keep_np[b, h], want_idx), (b, h)
+            keys, vals = O.draft_kv_rows("token_drop", k_full=O.bf16_to_f64(k[b, h]), v_full=O.bf16_to_f64(v[b, h]),
+                                         keep_idx=want_idx, tail_k=O.bf16_to_f64(tk[b, h]),
+                                         tail_v=O.bf16_to_f64(tv[b, h]))
+            ref = O.draft_attention_unit(O.bf16_to_f64(q[b, h * g:(h + 1) * g]), keys, vals, scale)
+            assert_close(got[b, h * g:(h + 1) * g], ref, f"select+drop b{b} h{h}")
