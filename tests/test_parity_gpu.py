@@ -278,17 +278,20 @@ def test_verify_prefill_causal():
         assert_close(got[0, h * g:(h + 1) * g], ref, f"prefill h{h}")
 
 
-def test_verify_ragged_context_lengths():
-    """Each sequence of the batch has its own context length; the cache rows after
-    a sequence's ctx_len + n_q hold large values that must not leak into it."""
+@pytest.mark.parametrize("ctx,D,g", [([600, 523, 17], 128, 4), ([0, 611, 1], 128, 8), ([0, 0, 40], 64, 2)],
+                         ids=["ragged", "empty_and_one_g8", "empty_d64"])
+def test_verify_ragged_context_lengths(ctx, D, g):
+    """Each sequence of the batch has its own context length (0 included: only
+    the new rows, causally); the cache rows after a sequence's ctx_len + n_q
+    hold large values that must not leak into it."""
     import torch
     vc = _vc()
     from compressed_kv_draft_amd.workload import bf16_dev
     from synth.gen import f32_to_bf16_bits
-    print("[case] verify ragged ctx_len", flush=True)
-    rng = np.random.default_rng(11)
-    B, Hq, Hkv, D, n_q, L_cap = 3, 8, 2, 128, 9, 700
-    ctx = [600, 523, 17]
+    print(f"[case] verify ragged ctx_len {ctx} D={D} g={g}", flush=True)
+    rng = np.random.default_rng(11 + D + g)
+    B, Hkv, n_q, L_cap = 3, 2, 9, 700
+    Hq = g * Hkv
     k = rng.standard_normal((B, Hkv, L_cap, D)).astype(np.float32)
     v = rng.standard_normal((B, Hkv, L_cap, D)).astype(np.float32)
     for b in range(B):
@@ -300,7 +303,6 @@ def test_verify_ragged_context_lengths():
     ctx_t = torch.tensor(ctx, dtype=torch.int32, device="cuda")
     scale = O.scale_for(D)
     got = vc.verify_attn(bf16_dev(qb, "cuda"), full, ctx_t, max(ctx), Hkv, scale).cpu().numpy()
-    g = Hq // Hkv
     for b in range(B):
         n = ctx[b] + n_q
         for h in range(Hkv):
