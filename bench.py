@@ -340,8 +340,20 @@ def cpu_baseline(w, dw, n_accept_sum, units):
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    import compressed_kv_draft_amd.workload as WL
+    round_bytes = sum(WL.draft_step_bytes(w, j) for j in range(w.k)) + WL.verify_bytes(w)
     return {"value": (n_accept_sum + w.B) / full, "unit": "verified tokens/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model,
+            "effective_GBps": round(round_bytes / full / 1e9, 3),
             "sample": f"{len(picks)} of {w.B * w.Hkv} (batch, kv-head) units, {w.k} draft steps + verify, "
                       f"fp64 numpy, {dt:.1f} s measured, scaled x{(w.B * w.Hkv) / len(picks):.0f}"}
 
