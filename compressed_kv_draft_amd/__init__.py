@@ -4,7 +4,8 @@ Importing the package loads libvc.so (built in place by ``build.py``) and fails
 loudly if it is missing: every step of the path runs in its HIP kernels.
 """
 from ._lib import (  # noqa: F401
-    LIB, VcError, Compressed, Tail, FullKV, version, quantize_kv, quantize_blocks, identity_cache, token_drop_cache,
+    LIB, VcError, Compressed, Tail, FullKV, version, quantize_kv, quantize_blocks, empty_quant, pack_quant, unpack_quant,
+    identity_cache, token_drop_cache,
     select_top_m,
     debug_dequant, draft_ws_bytes, draft_attn, verify_ws_bytes, verify_attn, verify_range_parts,
     verify_attn_range, verify_merge, argmax, accept,

@@ -45,6 +45,10 @@ EXPORTS = {
     "vc_quantize_kv": (c_int, [c_void, c_void, c_int, c_int, c_int, c_int, ctypes.POINTER(VcKvComp), c_void]),
     "vc_quantize_blocks": (c_int, [c_void, c_void, c_int, c_int, c_int, c_int, c_int, c_int,
                                    ctypes.POINTER(VcKvComp), c_int, c_void]),
+    "vc_pack_quant": (c_int, [c_void, c_void, c_void, c_void, c_int, c_int, c_int, c_int, ctypes.POINTER(VcKvComp),
+                              c_int, c_void]),
+    "vc_unpack_quant": (c_int, [ctypes.POINTER(VcKvComp), c_int, c_int, c_int, c_void, c_void, c_void, c_void,
+                                c_void]),
     "vc_select_top_m": (c_int, [c_void, c_int, c_int, c_int, c_void, c_void]),
     "vc_sched_accept_rate": (ctypes.c_double, [ctypes.c_longlong, ctypes.c_longlong]),
     "vc_sched_expected_tokens": (ctypes.c_double, [ctypes.c_double, c_int]),
@@ -173,6 +177,57 @@ def quantize_blocks(k_src: torch.Tensor, v_src: torch.Tensor, comp: Compressed, 
     if append:
         comp.set_n_quant(comp.desc.n_quant + 32 * n_blocks)
     return comp
+
+
+def empty_quant(B: int, Hkv: int, D: int, bits: int, capacity: int, device) -> Compressed:
+    """A QUANT cache (internal form) with room for `capacity` rows per (batch, kv-head)
+    and no live rows yet; fill it with pack_quant, quantize_blocks or set_n_quant."""
+    if capacity % 32 or capacity < 0:
+        raise VcError(f"capacity={capacity} must be a non-negative multiple of 32")
+    rb = D * bits // 8
+    t = dict(bits=bits, n_quant=0, q_cap=capacity,
+             k_codes=torch.empty((B, Hkv, capacity, rb), dtype=torch.uint8, device=device),
+             v_codes=torch.empty((B, Hkv, capacity, rb), dtype=torch.uint8, device=device),
+             k_meta=torch.empty((B, Hkv, capacity // 32, 2, D), dtype=torch.float16, device=device),
+             v_meta=torch.empty((B, Hkv, capacity // 32, D // 32, 32, 2), dtype=torch.float16, device=device))
+    return Compressed("quant", **t)
+
+
+def pack_quant(k_codes: torch.Tensor, v_codes: torch.Tensor, k_meta: torch.Tensor, v_meta: torch.Tensor,
+               comp: Compressed, dst_block: int | None = None, stream=None) -> Compressed:
+    """Canonical QUANT arrays (device): k_codes/v_codes u8 [B, Hkv, n, D*bits/8],
+    k_meta f16 [B, Hkv, n/32, D, 2] and v_meta f16 [B, Hkv, n, D/32, 2] ({scale, zero}
+    pairs) into blocks [dst_block, dst_block + n/32) of comp.  dst_block None appends
+    after the live rows and raises comp's n_quant by n."""
+    B, Hkv, n, rb = k_codes.shape
+    D = k_meta.shape[3]
+    for t, dt in ((k_codes, torch.uint8), (v_codes, torch.uint8), (k_meta, torch.float16), (v_meta, torch.float16)):
+        if t.dtype != dt or not t.is_contiguous():
+            raise VcError("vc_pack_quant: canonical arrays must be contiguous u8 codes and f16 metadata")
+    append = dst_block is None
+    if append:
+        dst_block = comp.desc.n_quant // 32
+    rc = LIB.vc_pack_quant(_ptr(k_codes), _ptr(v_codes), _ptr(k_meta), _ptr(v_meta), B, Hkv, n, D,
+                           ctypes.byref(comp.desc), int(dst_block), _stream(stream))
+    _check(rc, "vc_pack_quant")
+    if append:
+        comp.set_n_quant(comp.desc.n_quant + n)
+    return comp
+
+
+def unpack_quant(comp: Compressed, B: int, Hkv: int, D: int, stream=None):
+    """Live rows of a QUANT cache in canonical form: (k_codes, v_codes, k_meta, v_meta)
+    with the shapes pack_quant takes."""
+    n, bits = comp.desc.n_quant, comp.desc.bits
+    dev = comp.t["k_codes"].device
+    kc = torch.empty((B, Hkv, n, D * bits // 8), dtype=torch.uint8, device=dev)
+    vcd = torch.empty_like(kc)
+    km = torch.empty((B, Hkv, n // 32, D, 2), dtype=torch.float16, device=dev)
+    vm = torch.empty((B, Hkv, n, D // 32, 2), dtype=torch.float16, device=dev)
+    rc = LIB.vc_unpack_quant(ctypes.byref(comp.desc), B, Hkv, D, _ptr(kc), _ptr(vcd), _ptr(km), _ptr(vm),
+                             _stream(stream))
+    _check(rc, "vc_unpack_quant")
+    return kc, vcd, km, vm
 
 
 def identity_cache(k_full: torch.Tensor, v_full: torch.Tensor, L_full: int) -> Compressed:

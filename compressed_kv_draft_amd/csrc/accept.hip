@@ -1,9 +1,10 @@
 // Greedy token selection and prefix acceptance.
 //
-// [VC Core Algorithm: tokens are accepted up to the first mismatch with the
-//  full-KV prediction; if every draft matches, one more ("bonus") token is
-//  accepted; the loop restarts from the last accepted token.
-//  VC Experimental Results: the output equals full-KV greedy decoding.]
+// [VC Core Algorithm: acceptance; VC Experimental Results: identical output
+//  under greedy decoding]  The rule: n is the position of the first draft that
+//  differs from the verifier's greedy token at that position (k when none
+//  does); the drafts before it are kept and the verifier's token at n follows
+//  them, so every round emits n + 1 tokens and the next round starts there.
 #include "vc_common.h"
 
 namespace vc {

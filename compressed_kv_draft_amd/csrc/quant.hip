@@ -5,6 +5,7 @@
 //  compressors; VC Architecture Support: KIVI behind the uniform interface]
 // The page gives no formula; the quantiser is the plain min/max one, every
 // step an IEEE fp32 operation with round-to-nearest-even (no contraction).
+#include "mfma.h"
 #include "vc_common.h"
 
 namespace vc {
@@ -160,6 +161,92 @@ __global__ void dequant_kernel(const uint8_t* __restrict__ codes, const H2* __re
   out[idx] = fmaf((float)c, s, z);
 }
 
+// Conversions between the canonical (dense) QUANT format and the internal
+// one.  Canonical, per (batch, kv-head) unit of n rows:
+//   K and V codes  u8 [n][D*bits/8], token rows packed along D (4-bit: channel
+//                  2i low nibble of byte i; 2-bit: channel i at bit 2 (i % 4))
+//   K meta         f16x2 {scale, zero} [n/32][D]   (a pair per 32 tokens of a channel)
+//   V meta         f16x2 {scale, zero} [n][D/32]   (a pair per 32 channels of a token)
+// Internal: K codes as canonical; V codes tiled (vcode_locate); K meta in pair
+// order (kmeta_pos); V meta in score-tile token order (vmeta_slot).  One thread
+// per output item; part = blockIdx.z selects K codes (16-byte chunks), V
+// codes (bytes), K meta, V meta (pairs).
+struct PackArgs {
+  int D, bits, n32, cap32, blk0;  // canonical blocks n32; internal blocks per unit cap32; first block blk0
+  uint8_t* ck;                    // canonical side (read when packing, written when unpacking)
+  uint8_t* cv;
+  H2* ckm;
+  H2* cvm;
+  uint8_t* ik;                    // internal side (written when packing, read when unpacking)
+  uint8_t* iv;
+  H2* ikm;
+  H2* ivm;
+};
+
+// pack = true: canonical -> internal (writes the internal arrays, blocks
+// blk0 .. blk0 + n32 - 1); false: internal blocks blk0 .. -> canonical.
+template <bool PACK>
+__global__ void convert_quant_kernel(PackArgs a) {
+  const int unit = blockIdx.y, part = blockIdx.z;
+  const int D = a.D, bits = a.bits, G = D / 32;
+  const int row_bytes = D * bits / 8, blk_bytes = 32 * row_bytes;
+  const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t cblk0 = (size_t)unit * a.n32;                // first canonical block of the unit
+  const size_t iblk0 = (size_t)unit * a.cap32 + a.blk0;     // first internal block of the unit
+  if (part == 0) {  // K codes: the same bytes, 16 at a time
+    const size_t n16 = (size_t)a.n32 * blk_bytes / 16;
+    if (gid >= n16) return;
+    const u32x4* src = reinterpret_cast<const u32x4*>(PACK ? a.ck + cblk0 * blk_bytes : a.ik + iblk0 * blk_bytes);
+    u32x4* dst = reinterpret_cast<u32x4*>(PACK ? a.ik + iblk0 * blk_bytes : a.ck + cblk0 * blk_bytes);
+    dst[gid] = src[gid];
+  } else if (part == 1) {  // V codes: one internal byte (pack) or canonical byte (unpack)
+    if (gid >= (size_t)a.n32 * blk_bytes) return;
+    const int blk = (int)(gid / blk_bytes), byte = (int)(gid % blk_bytes);
+    const int per = 8 / bits;
+    const uint32_t mask = (1u << bits) - 1u;
+    uint32_t v = 0;
+    if (PACK) {
+      const uint8_t* rows = a.cv + (cblk0 + blk) * blk_bytes;
+      for (int k = 0; k < per; ++k) {
+        int tau, c;
+        vcode_inverse(D, bits, byte, k, tau, c);
+        const uint32_t code = (rows[tau * row_bytes + c / per] >> (bits * (c % per))) & mask;
+        v |= code << (bits * k);
+      }
+      a.iv[(iblk0 + blk) * blk_bytes + byte] = (uint8_t)v;
+    } else {
+      const uint8_t* tiled = a.iv + (iblk0 + blk) * blk_bytes;
+      const int tau = byte / row_bytes, c0 = (byte % row_bytes) * per;
+      for (int k = 0; k < per; ++k) {
+        int tb, sh;
+        vcode_locate(D, bits, tau, c0 + k, tb, sh);
+        v |= ((tiled[tb] >> sh) & mask) << (bits * k);
+      }
+      a.cv[(cblk0 + blk) * blk_bytes + byte] = (uint8_t)v;
+    }
+  } else if (part == 2) {  // K meta: one (block, channel) pair
+    if (gid >= (size_t)a.n32 * D) return;
+    const int blk = (int)(gid / D), c = (int)(gid % D);
+    _Float16* plane = reinterpret_cast<_Float16*>(a.ikm + (iblk0 + blk) * D);
+    const int pos = kmeta_pos(D, bits, c);
+    H2& canon = a.ckm[(cblk0 + blk) * D + c];
+    if (PACK) {
+      plane[pos] = canon.s;
+      plane[D + pos] = canon.z;
+    } else {
+      canon.s = plane[pos];
+      canon.z = plane[D + pos];
+    }
+  } else {  // V meta: one (token, channel group) pair
+    if (gid >= (size_t)a.n32 * 32 * G) return;
+    const int t = (int)(gid / G), grp = (int)(gid % G);
+    const size_t ci = (cblk0 * 32 + t) * G + grp;
+    const size_t ii = ((iblk0 + t / 32) * G + grp) * 32 + vmeta_slot(t % 32);
+    if (PACK) a.ivm[ii] = a.cvm[ci];
+    else a.cvm[ci] = a.ivm[ii];
+  }
+}
+
 }  // namespace
 }  // namespace vc
 
@@ -248,4 +335,62 @@ extern "C" int vc_debug_dequant(const vc_kv_comp* comp, int B, int Hkv, int D, i
   dequant_kernel<<<(n + 255) / 256, 256, 0, stream>>>(codes, meta, comp->bits, nq, D, which, out);
   VC_HIP(hipGetLastError());
   return VC_OK;
+}
+
+// Shared validation and launch of the canonical <-> internal conversion.
+static int convert_quant(const char* fn, bool pack, const uint8_t* k_codes, const uint8_t* v_codes,
+                         const void* k_meta, const void* v_meta, int B, int Hkv, int n, int D,
+                         const vc_kv_comp* comp, int blk0, hipStream_t stream) {
+  VC_CHECK(comp != nullptr, "%s: descriptor is NULL", fn);
+  VC_CHECK(comp->kind == VC_KV_QUANT, "%s: kind must be VC_KV_QUANT", fn);
+  VC_CHECK(comp->bits == 2 || comp->bits == 4, "%s: bits must be 2 or 4 (got %d)", fn, comp->bits);
+  VC_CHECK(B > 0 && Hkv > 0, "%s: bad B/Hkv (%d,%d)", fn, B, Hkv);
+  if (D != 64 && D != 128) return fail(VC_ERR_UNSUPPORTED, "%s: D=%d not in {64,128}", fn, D);
+  const int cap = quant_cap(comp);
+  VC_CHECK(cap >= 0 && cap % 32 == 0, "%s: q_cap=%d must be a multiple of 32", fn, cap);
+  VC_CHECK(n >= 0 && n % 32 == 0, "%s: rows n=%d must be a multiple of 32", fn, n);
+  VC_CHECK(blk0 >= 0 && 32LL * blk0 + n <= cap, "%s: blocks [%d, %d) outside the %d-row cache", fn, blk0,
+           blk0 + n / 32, cap);
+  if (n == 0) return VC_OK;
+  VC_CHECK(k_codes && v_codes && k_meta && v_meta, "%s: null canonical array", fn);
+  VC_CHECK(comp->k_codes && comp->v_codes && comp->k_meta && comp->v_meta, "%s: null cache array", fn);
+  VC_CHECK(aligned(k_codes, 16) && aligned(comp->k_codes, 16) && aligned(k_meta, 4) && aligned(v_meta, 4) &&
+               aligned(comp->k_meta, 4) && aligned(comp->v_meta, 4),
+           "%s: K codes must be 16-byte aligned and metadata 4-byte aligned", fn);
+  PackArgs a{};
+  a.D = D;
+  a.bits = comp->bits;
+  a.n32 = n / 32;
+  a.cap32 = cap / 32;
+  a.blk0 = blk0;
+  a.ck = const_cast<uint8_t*>(k_codes);
+  a.cv = const_cast<uint8_t*>(v_codes);
+  a.ckm = static_cast<H2*>(const_cast<void*>(k_meta));
+  a.cvm = static_cast<H2*>(const_cast<void*>(v_meta));
+  a.ik = const_cast<uint8_t*>(comp->k_codes);
+  a.iv = const_cast<uint8_t*>(comp->v_codes);
+  a.ikm = reinterpret_cast<H2*>(const_cast<void*>(comp->k_meta));
+  a.ivm = reinterpret_cast<H2*>(const_cast<void*>(comp->v_meta));
+  // the largest part: V code bytes (n * D * bits / 8) >= pairs and 16-byte chunks
+  const size_t items = (size_t)n * D * comp->bits / 8;
+  VC_CHECK((items + 255) / 256 < (1u << 31), "%s: too many rows", fn);
+  const dim3 grid((unsigned)((items + 255) / 256), B * Hkv, 4);
+  if (pack) convert_quant_kernel<true><<<grid, 256, 0, stream>>>(a);
+  else convert_quant_kernel<false><<<grid, 256, 0, stream>>>(a);
+  VC_HIP(hipGetLastError());
+  return VC_OK;
+}
+
+extern "C" int vc_pack_quant(const uint8_t* k_codes, const uint8_t* v_codes, const void* k_meta,
+                             const void* v_meta, int B, int Hkv, int n, int D, const vc_kv_comp* out,
+                             int dst_block, hipStream_t stream) {
+  return convert_quant("vc_pack_quant", true, k_codes, v_codes, k_meta, v_meta, B, Hkv, n, D, out, dst_block,
+                       stream);
+}
+
+extern "C" int vc_unpack_quant(const vc_kv_comp* in, int B, int Hkv, int D, uint8_t* k_codes, uint8_t* v_codes,
+                               void* k_meta, void* v_meta, hipStream_t stream) {
+  VC_CHECK(in != nullptr, "vc_unpack_quant: descriptor is NULL");
+  return convert_quant("vc_unpack_quant", false, k_codes, v_codes, k_meta, v_meta, B, Hkv, in->n_quant, D, in, 0,
+                       stream);
 }

@@ -55,6 +55,7 @@ struct VerifyArgs {
   int rowgroups, tiles_per_group;  // query tiles per workgroup <= NW * MT
   int splits, keys_per_split;
   int key_begin, key_limit;        // keys [key_begin, key_limit) of every sequence, clipped to ctx_len + n_q
+  int key_lo;                      // keys below key_lo are masked (key_begin rounded down for paged loads)
   int write_partials;              // 1: always write split partials to ws (range calls), never the output
   int n_su;                        // splits * units
   float scale_log2;
@@ -161,7 +162,11 @@ __global__ __launch_bounds__(64 * NW) void verify_mfma_kernel(VerifyArgs a) {
   // s = (r * LW + wave) * 64 + lane
   // of the tile, which holds 16-byte chunk (s % CPR) ^ swz(key) of key row
   // key = s / CPR: the XOR swizzle makes the operand reads below conflict-free.
-  // The rows of one load instruction lie in one page (pages hold >= 8 rows).
+  // One load instruction covers 64 / CPR consecutive rows (4 or 8) starting at
+  // a multiple of that count: tiles start at key_begin + 32 n and a paged
+  // call's key_begin is a multiple of 8, so those rows lie in one page (pages
+  // hold a power-of-two count >= 8 of rows) and one scalar page lookup serves
+  // the whole instruction.
   const uint32_t lds0 = lds_address(smem);
   const unsigned char* kv8 = reinterpret_cast<const unsigned char*>(a.k);
   const unsigned char* vv8 = reinterpret_cast<const unsigned char*>(a.v);
@@ -292,8 +297,9 @@ __global__ __launch_bounds__(64 * NW) void verify_mfma_kernel(VerifyArgs a) {
         for (int i = 0; i < LIVE; ++i) s[i][h] = mfma_bf16(kcur, qb[i][ks], s[i][h]);
         kcur = knext;
       }
-      // mask only tiles that reach the drafted rows or the end of the range
-      const bool need_mask = t0 + kKT > ctx || t0 + kKT > ke;
+      // mask only tiles that reach the drafted rows, the end of the range, or
+      // start below its first key
+      const bool need_mask = t0 + kKT > ctx || t0 + kKT > ke || t0 < a.key_lo;
       f16x8 A[LIVE > 0 ? LIVE : 1];
 #pragma unroll
       for (int i = 0; i < LIVE; ++i) {
@@ -303,13 +309,14 @@ __global__ __launch_bounds__(64 * NW) void verify_mfma_kernel(VerifyArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) xv[4 * h + e] = fmaf(s[i][h][e], a.scale_log2, -mu[i]);
         if (need_mask) {
-          // key t0 + 16h + 4q + e is visible iff 16h + e <= lim
+          // key t0 + 16h + 4q + e is visible iff lo <= 16h + e <= lim
           const int lim = min(rlim[i], ke - 1) - t0 - 4 * quad;
+          const int lo = a.key_lo - t0 - 4 * quad;
 #pragma unroll
           for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (16 * h + e > lim) xv[4 * h + e] = kNegInf;
+              if (16 * h + e > lim || 16 * h + e < lo) xv[4 * h + e] = kNegInf;
         }
         float tl = xv[0];
 #pragma unroll
@@ -518,6 +525,9 @@ size_t verify_ws_need(int B, int Hq, int n_q, int D, int splits) {
   return need < 256 ? 256 : need;
 }
 
+// First row a call over keys [key_begin, ...) reads: rounded down to a multiple of 8.
+inline int range_base(int key_begin) { return key_begin & ~7; }
+
 // Resident workgroups per CU the partial layout of a range call is planned
 // for: a fixed number per kernel shape (2 wavefronts per SIMD), so that
 // vc_verify_range_parts needs no device and always agrees with the call.
@@ -570,10 +580,15 @@ int verify_launch(const char* fn, const void* q, const vc_kv_full* kv, const int
   a.R = a.g * n_q;
   a.NT = (a.R + 15) / 16;
   a.scale_log2 = scale * kLog2e;
-  a.key_begin = key_begin;
+  // the cache is read from the 8-aligned row at or below key_begin (the rows
+  // in between are masked), so that no load instruction of a paged cache
+  // spans two pages; contiguous caches take the same plan, so that
+  // vc_verify_range_parts needs no cache description
+  a.key_lo = key_begin;
+  a.key_begin = range_base(key_begin);
   a.key_limit = key_limit;
   a.write_partials = parts != nullptr ? 1 : 0;
-  const int keys = key_limit - key_begin;
+  const int keys = key_limit - a.key_begin;
   Plan p = plan_verify(B, Hq, Hkv, n_q, keys, 8);
   const bool paged = kv->page_table != nullptr;
   const VerifyKernel kern = D == 128 ? (paged ? pick<128, true>(p.mt, p.nw) : pick<128, false>(p.mt, p.nw))
@@ -629,8 +644,9 @@ extern "C" int vc_verify_range_parts(int B, int Hq, int Hkv, int D, int n_q, int
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || (D != 64 && D != 128) || n_q <= 0 || key_begin < 0 ||
       key_end <= key_begin)
     return 0;
-  const Plan p = plan_verify(B, Hq, Hkv, n_q, key_end - key_begin, 8);
-  return plan_verify(B, Hq, Hkv, n_q, key_end - key_begin, range_wpc(p)).splits;
+  const int keys = key_end - range_base(key_begin);
+  const Plan p = plan_verify(B, Hq, Hkv, n_q, keys, 8);
+  return plan_verify(B, Hq, Hkv, n_q, keys, range_wpc(p)).splits;
 }
 
 extern "C" int vc_verify_attn_range(const void* q, const vc_kv_full* kv, const int32_t* ctx_len, int max_ctx,

@@ -17,8 +17,11 @@
  *  - Pointers marked "device" must be device memory on the current HIP device;
  *    "host" pointers are read during the call only.  The caller owns every
  *    buffer; the library never allocates, frees or retains device memory.
- *  - Calls are asynchronous on the given stream and never synchronise.  They
- *    are reentrant; two calls that share a workspace must be stream-ordered.
+ *  - Calls are asynchronous on the given stream: they enqueue work and return
+ *    without waiting for the device.  The one exception is
+ *    vc_prefetch_full_kv, whose host-side gather blocks the calling thread and
+ *    may wait on the host for a staging event (see there).  Calls are
+ *    reentrant; two calls that share a workspace must be stream-ordered.
  *  - bf16 = IEEE bfloat16 bit patterns; f16 = IEEE binary16; all tensors are
  *    dense row-major with the shapes given.
  *  - Heads: query head h reads KV head h / (Hq / Hkv) (contiguous GQA groups).
@@ -51,8 +54,25 @@ extern "C" {
 #define VC_KV_TOKEN_DROP 2 /* a kept subset of context rows, by index      */
 
 /*
- * QUANT layout (per (b, kv-head) slices are consecutive; each holds Q = q_cap
- * rows, q_cap = n_quant when the field is 0, of which [0, n_quant) are live):
+ * QUANT caches exist in two forms.
+ *
+ * Canonical form (what a compressor produces; vc_pack_quant reads it and
+ * vc_unpack_quant writes it), per (b, kv-head) unit of n rows, units
+ * consecutive, dense:
+ *   K codes  u8 [B][Hkv][n][D*bits/8]  token rows packed along D: 4-bit:
+ *            channel 2i in the low nibble of byte i, 2i+1 in the high nibble;
+ *            2-bit: channel i at bit 2*(i%4) of byte i/4
+ *   V codes  u8 [B][Hkv][n][D*bits/8]  the same packing
+ *   K meta   f16x2 {scale, zero} [B][Hkv][n/32][D]  one pair per group of 32
+ *            tokens of one channel
+ *   V meta   f16x2 {scale, zero} [B][Hkv][n][D/32]  one pair per group of 32
+ *            channels of one token
+ *   value = fp32(code * scale + zero), a single rounding.
+ *
+ * Internal form (what vc_draft_attn reads; written by vc_quantize_kv,
+ * vc_quantize_blocks and vc_pack_quant).  Per (b, kv-head) slices are
+ * consecutive; each holds Q = q_cap rows, q_cap = n_quant when the field is
+ * 0, of which [0, n_quant) are live:
  *   k_codes  u8 [B][Hkv][Q][D*bits/8]  codes of token t packed along D:
  *            4-bit: channel 2i in the low nibble of byte i, 2i+1 in the high
  *            nibble; 2-bit: channel i at bit 2*(i%4) of byte i/4.
@@ -64,7 +84,7 @@ extern "C" {
  *              pi = i * (D/16) + ct, dword = pi / (16/bits), j = pi % (16/bits),
  *              bit = bits * j + 16 * hf,
  *              byte = lane * (D*bits/16) + 4 * dword + bit / 8,
- *            code at bit (bit % 8) of that byte.  vc_quantize_kv writes it.
+ *            code at bit (bit % 8) of that byte.
  *   k_meta   f16 [B][Hkv][Q/32][2][D]  per 32-token block, a plane of
  *            the scales and then a plane of the zeros of the groups formed by
  *            the block's 32 tokens of one channel, each plane in pair order:
@@ -161,9 +181,10 @@ int vc_quantize_kv(const void* k_src, const void* v_src, int B, int Hkv, int L_c
 /*
  * vc_quantize_blocks — grow a QUANT cache by whole 32-token blocks: the rows
  * that leave the exact recent window are quantised into the next blocks of
- * the cache.  [VC Architecture Support: KIVI keeps a full-precision recent
- * window and quantises tokens that leave it; VC Problem Statement: the
- * compressed cache is kept up to date as decoding proceeds]
+ * the cache.  [VC Architecture Support: KIVI is one of the quantisers the
+ * uniform compressor interface names]  The pages do not say how a quantised
+ * cache grows during decoding; moving whole 32-token blocks out of an exact
+ * recent window is this library's rule.
  * Source rows [src_row0, src_row0 + 32 * n_blocks) of every (b, kv-head) of
  * k_src / v_src (device bf16 [B][Hkv][src_rows][D]) become cache blocks
  * [dst_block, dst_block + n_blocks) of out, with the same per-group
@@ -179,6 +200,31 @@ int vc_quantize_kv(const void* k_src, const void* v_src, int B, int Hkv, int L_c
  */
 int vc_quantize_blocks(const void* k_src, const void* v_src, int B, int Hkv, int src_rows, int D, int src_row0,
                        int n_blocks, const vc_kv_comp* out, int dst_block, hipStream_t stream);
+
+/*
+ * vc_pack_quant — the compressor-facing side of the uniform interface: turn a
+ * QUANT cache in canonical form (k_codes, v_codes, k_meta, v_meta: device, n
+ * rows per unit, layouts above) into blocks [dst_block, dst_block + n/32) of
+ * the internal form that `out` describes (its kind, bits and q_cap are read;
+ * its arrays are written).  [VC Architecture Support: a uniform compressor
+ * interface admits existing quantisation methods without changes to the
+ * scheduling or verification logic]  A compressor that produces the
+ * canonical form can feed vc_draft_attn through this call; quantising with
+ * vc_quantize_kv gives the same bytes as packing the canonical form of the
+ * same quantisation.  n % 32 == 0 and 32 * dst_block + n <= q_cap (or
+ * n_quant when q_cap is 0); n == 0 is a no-op.  out->n_quant is not changed.
+ * Canonical K codes and the internal K codes must be 16-byte aligned, all
+ * metadata 4-byte aligned.  Errors: VC_ERR_INVALID (bad kind/bits, range,
+ * NULL or misaligned pointer), VC_ERR_UNSUPPORTED (D not in {64, 128}).
+ * One launch on `stream`; nothing is allocated.
+ *
+ * vc_unpack_quant — the inverse: rows [0, in->n_quant) of the internal form
+ * into canonical arrays of n_quant rows per unit.  Same rules.
+ */
+int vc_pack_quant(const uint8_t* k_codes, const uint8_t* v_codes, const void* k_meta, const void* v_meta,
+                  int B, int Hkv, int n, int D, const vc_kv_comp* out, int dst_block, hipStream_t stream);
+int vc_unpack_quant(const vc_kv_comp* in, int B, int Hkv, int D, uint8_t* k_codes, uint8_t* v_codes,
+                    void* k_meta, void* v_meta, hipStream_t stream);
 
 /*
  * vc_select_top_m — the token-dropping compressor's selection: for each of
@@ -259,8 +305,10 @@ int vc_verify_attn(const void* q, const vc_kv_full* kv, const int32_t* ctx_len, 
  *
  * vc_verify_attn_range — keys [key_begin, key_end) of every sequence, clipped
  * to the causal limit ctx_len[b] + j of query position j.  Arguments as in
- * vc_verify_attn; only the pages (or rows) of the range are read, so the
- * rest of a paged cache may still be in flight.  Writes
+ * vc_verify_attn.  Reads start at the multiple of 8 at or below key_begin
+ * (the rows before key_begin are masked out); that row lies in key_begin's
+ * page, so only the pages holding rows of the range are read and the rest of
+ * a paged cache may still be in flight.  key_begin need not be aligned.  Writes
  * vc_verify_range_parts(B, Hq, Hkv, D, n_q, key_begin, key_end) partial
  * slots to parts (device fp32, 16-byte aligned), each [B*Hq*n_q][D + 2]:
  * per query row the unnormalised sum o[0..D) of 2^(s - m) v over its keys,
@@ -289,9 +337,10 @@ int vc_verify_merge(const float* parts, int n_parts, int B, int Hq, int n_q, int
 int vc_argmax(const float* logits, int rows, int V, int32_t* ids, hipStream_t stream);
 
 /*
- * vc_accept — greedy acceptance.  [VC Core Algorithm: tokens are accepted up
- * to the first mismatch; if all drafts match, a bonus token is accepted; the
- * loop repeats from the last accepted token]
+ * vc_accept — greedy acceptance.  [VC Core Algorithm: acceptance]  Each
+ * sequence keeps its drafts up to the first one the verifier disagrees with,
+ * then the verifier's own token; with no disagreement that token is the
+ * bonus.
  *   draft_ids      device int32 [B][k]      d_0 .. d_{k-1}
  *   verify_logits  device fp32 [B][k+1][V]  logits of verify positions 0..k
  *   out_ids        device int32 [B][k+1]    d_0..d_{n-1}, y_n, then -1

@@ -11,7 +11,10 @@ English and Korean versions; cited as [VC <section>]) and "CacheGen: KV Cache
 Compression and Streaming ..." (context only).  Where the pages are silent the
 function states the reading it takes.
 
-Parity status: every function is pinned by ``tests/test_oracle.py`` to closed
-forms, invariants or brute force; none is "parity unpinned".
+Parity status: every function has a pin of its own in ``tests/test_oracle.py``
+(closed forms, invariants, brute force or hand-worked values; ``dequant_v``
+and ``logits`` by hand-worked examples), each shown to fail on planted
+mistakes; none is "parity unpinned".  The oracle holds only the method's
+canonical data forms, none of the kernels' internal layouts.
 """
 from .vc_oracle import *  # noqa: F401,F403

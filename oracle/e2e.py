@@ -1,11 +1,12 @@
 """fp64 reference of the end-to-end draft-then-verify loop on a tiny decoder (test infrastructure only).
 
-[VC Core Algorithm] the draft model is the target model itself reading a
-compressed cache KV_comp; a single forward pass over the full cache KV_full
-verifies the k drafted tokens; tokens are accepted up to the first mismatch
-plus one verifier token; the loop repeats from the last accepted token.
-[VC Experimental Results] under greedy decoding the output equals that of the
-target model run with its full cache.
+[VC Core Algorithm] drafting runs the target model itself over a compressed
+cache KV_comp; one forward pass over the full cache KV_full checks the k
+drafts together; the drafts before the first one that differs from the
+verifier's greedy token are kept, followed by the verifier's token at that
+position, and the next round starts from there.  [VC Experimental Results]
+with greedy decoding the loop emits exactly what the target model emits with
+its full cache.
 
 Model (the pages name none; readings):
   * Llama-style pre-norm decoder: x += O(attn(RMSNorm(x))); x += SwiGLU(RMSNorm(x));

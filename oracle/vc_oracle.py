@@ -105,6 +105,9 @@ def dequant_k(codes: np.ndarray, s: np.ndarray, z: np.ndarray) -> np.ndarray:
 
 
 def dequant_v(codes: np.ndarray, s: np.ndarray, z: np.ndarray) -> np.ndarray:
+    """x' = fp32(code * s + z) with s, z the fp16 pair of the value's group: 32
+    consecutive channels of its own token (codes [n, D], s and z [n, D/32]).
+    Exact in fp64, rounded once to fp32, as for K."""
     n, D = codes.shape
     sf = np.repeat(f16_to_f64(s), GROUP, axis=1)
     zf = np.repeat(f16_to_f64(z), GROUP, axis=1)
@@ -122,76 +125,6 @@ def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
     for i in range(per):
         out |= c[:, :, i] << np.uint16(bits * i)
     return out.astype(np.uint8)
-
-
-def pack_v_codes_tiled(codes: np.ndarray, bits: int) -> np.ndarray:
-    """Pack V codes [n, D] (n % 32 == 0) into the tiled byte layout that the C
-    header (include/vc.h, QUANT layout, v_codes) defines; returns uint8
-    [n * D * bits / 8].  A pure permutation of the codes' bits, written from that
-    definition: token tau of each 32-token block and channel c go to
-      q = (tau % 16) // 4, e = tau % 4 + 4 (tau // 16), lane = 16 q + c % 16,
-      i = e // 2, hf = e % 2, ct = c // 16, pi = i (D / 16) + ct,
-      dword = pi // (16 / bits), j = pi % (16 / bits), bit = bits j + 16 hf,
-      byte = lane (D bits / 16) + 4 dword + bit // 8, shift = bit % 8."""
-    n, D = codes.shape
-    assert n % GROUP == 0
-    tau = np.arange(32)[:, None]
-    c = np.arange(D)[None, :]
-    q = (tau % 16) // 4
-    e = tau % 4 + 4 * (tau // 16)
-    lane = 16 * q + c % 16
-    i, hf, ct = e // 2, e % 2, c // 16
-    pi = i * (D // 16) + ct
-    ppd = 16 // bits
-    dword, j = pi // ppd, pi % ppd
-    bit = bits * j + 16 * hf
-    byte = lane * (D * bits // 16) + 4 * dword + bit // 8
-    shift = (bit % 8).astype(np.uint16)
-    nb = n // GROUP
-    blk_bytes = 4 * D * bits
-    out = np.zeros((nb, blk_bytes), dtype=np.uint16)
-    vals = codes.reshape(nb, 32, D).astype(np.uint16) << shift[None]
-    flat = (np.arange(nb)[:, None, None] * blk_bytes + byte[None]).reshape(-1)
-    np.bitwise_or.at(out.reshape(-1), flat, vals.reshape(-1))
-    return out.reshape(-1).astype(np.uint8)
-
-
-def pack_k_meta(s: np.ndarray, z: np.ndarray, bits: int) -> np.ndarray:
-    """K scales and zeros [n/32, D] (fp16) into the C header's k_meta layout
-    (include/vc.h, QUANT layout): per block a scale plane then a zero plane,
-    channel c of each at f16 index
-      quad = c // (D/4), r = c % (D/4), cpd = 32 // bits, ppd = cpd // 2,
-      d = r // cpd, h = (r % cpd) // ppd, j = r % ppd, pi = d ppd + j,
-      pos = 2 ((quad (D/32) + pi // 4) 4 + pi % 4) + h.
-    Returns the raw fp16 bit patterns, uint16 [n/32, 2, D]."""
-    nb, D = s.shape
-    cpd = 32 // bits
-    ppd = cpd // 2
-    out = np.zeros((nb, 2, D), dtype=np.uint16)
-    for c in range(D):
-        quad, r = divmod(c, D // 4)
-        d, rem = divmod(r, cpd)
-        h, j = divmod(rem, ppd)
-        pi = d * ppd + j
-        pos = 2 * ((quad * (D // 32) + pi // 4) * 4 + pi % 4) + h
-        out[:, 0, pos] = s[:, c].view(np.uint16)
-        out[:, 1, pos] = z[:, c].view(np.uint16)
-    return out
-
-
-def pack_v_meta(s: np.ndarray, z: np.ndarray) -> np.ndarray:
-    """V scales and zeros [n, D/32] (fp16) into the header's v_meta layout:
-    [n/32][D/32 groups][32 slots]{scale, zero}, token tau of a block in slot
-    8 ((tau % 16) // 4) + tau % 4 + 4 (tau // 16).  uint16 [n/32, D/32, 32, 2]."""
-    n, G = s.shape
-    assert n % GROUP == 0
-    nb = n // GROUP
-    out = np.zeros((nb, G, 32, 2), dtype=np.uint16)
-    for tau in range(32):
-        slot = 8 * ((tau % 16) // 4) + tau % 4 + 4 * (tau // 16)
-        out[:, :, slot, 0] = s[tau::32].view(np.uint16)
-        out[:, :, slot, 1] = z[tau::32].view(np.uint16)
-    return out
 
 
 # ----------------------------------------------------------------------------
@@ -275,7 +208,10 @@ def verify_attention_unit(q: np.ndarray, k_all: np.ndarray, v_all: np.ndarray, L
 
 
 def logits(o_heads: np.ndarray, w: np.ndarray) -> np.ndarray:
-    """Vocab logits of one position: concat over heads (head-major) of o [Hq, D], times W [Hq*D, V]."""
+    """Vocab logits of one position: the head outputs o [Hq, D] laid end to end
+    head by head (head 0's D channels, then head 1's, ...), times W [Hq*D, V].
+    Reading: the workloads define the logits as the concatenated head outputs
+    times a vocabulary matrix; the pages give no formula."""
     return o_heads.reshape(-1) @ w
 
 

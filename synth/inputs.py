@@ -77,11 +77,11 @@ def pages_per_seq(w: Workload) -> int:
 
 
 def page_table(w: Workload) -> tuple[np.ndarray, int]:
-    """Shuffled table for the context pages of every sequence, then one fresh slot
-    per page that holds new rows (those pages live only on the device).
-    Returns (table [B, pages_per_seq], total slots)."""
+    """Shuffled table for the whole context pages of every sequence, then one
+    fresh slot per page that holds new rows (those pages live only on the
+    device; with L not a multiple of the page size the first of them also holds
+    the last context rows).  Returns (table [B, pages_per_seq], total slots)."""
     ctx_pages = w.L // w.page_tokens
-    assert w.L % w.page_tokens == 0
     n_ctx = w.B * ctx_pages
     perm = page_permutation(w.seed, n_ctx)
     pps = pages_per_seq(w)

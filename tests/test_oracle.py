@@ -136,10 +136,9 @@ def test_quant_blocks_are_independent():
     kb = [O.quantize_k(k[i:i + 32], bits) for i in range(0, n, 32)]
     vb = [O.quantize_v(v[i:i + 32], bits) for i in range(0, n, 32)]
     assert np.array_equal(O.pack_codes(c, bits), np.concatenate([O.pack_codes(b[0], bits) for b in kb]))
-    assert np.array_equal(O.pack_k_meta(s, z, bits), np.concatenate([O.pack_k_meta(b[1], b[2], bits) for b in kb]))
-    assert np.array_equal(O.pack_v_codes_tiled(cv, bits),
-                          np.concatenate([O.pack_v_codes_tiled(b[0], bits) for b in vb]))
-    assert np.array_equal(O.pack_v_meta(sv, zv), np.concatenate([O.pack_v_meta(b[1], b[2]) for b in vb]))
+    assert np.array_equal(s, np.concatenate([b[1] for b in kb])) and np.array_equal(z, np.concatenate([b[2] for b in kb]))
+    assert np.array_equal(O.pack_codes(cv, bits), np.concatenate([O.pack_codes(b[0], bits) for b in vb]))
+    assert np.array_equal(sv, np.concatenate([b[1] for b in vb])) and np.array_equal(zv, np.concatenate([b[2] for b in vb]))
     # and a block's K groups do see all of its 32 rows: changing one row moves them
     k2 = k.copy()
     k2[40] += 100.0
@@ -154,77 +153,6 @@ def test_pack_codes_bit_layout():
     assert list(O.pack_codes(c2, 2)[0]) == [0b00111001, 0xFF]
 
 
-def test_pack_v_tiled_positions_and_bijection():
-    """The tiled V layout (include/vc.h): hand-derived positions of single codes,
-    and every (token, channel) code lands on its own bits."""
-    D, bits = 128, 2
-    def where(tau, c, val=3):
-        codes = np.zeros((32, D), np.uint8)
-        codes[tau, c] = val
-        out = O.pack_v_codes_tiled(codes, bits)
-        nz = np.nonzero(out)[0]
-        assert len(nz) == 1
-        return int(nz[0]), int(out[nz[0]])
-    # tau 0, c 0: q 0, e 0, lane 0, pi 0 -> dword 0, bit 0
-    assert where(0, 0) == (0, 3)
-    # tau 1, c 0: e 1 -> hf 1 -> bit 16 -> byte 2
-    assert where(1, 0) == (2, 3)
-    # tau 17, c 16: q 0, e 5 -> i 2, hf 1; ct 1 -> pi 17 -> dword 2, j 1 -> bit 18 -> byte 10, shift 2
-    assert where(17, 16) == (10, 3 << 2)
-    # tau 6, c 37: q 1, e 2 -> i 1, hf 0; lane 16 + 5 = 21; ct 2 -> pi 10 -> dword 1, j 2 -> bit 4
-    assert where(6, 37) == (21 * 16 + 4, 3 << 4)
-    for D_, b_ in [(64, 2), (64, 4), (128, 2), (128, 4)]:
-        rng = np.random.default_rng(D_ + b_)
-        codes = rng.integers(0, 1 << b_, (64, D_)).astype(np.uint8)
-        packed = O.pack_v_codes_tiled(codes, b_)
-        assert packed.size == 64 * D_ * b_ // 8
-        # total bit population is preserved (no two codes share bits)
-        pop = lambda a: int(np.unpackbits(a.astype(np.uint8)).sum())
-        assert pop(packed) == pop(O.pack_codes(codes, b_))
-        # a permutation: each code value alone is found again
-        one = np.zeros_like(codes)
-        one[37, D_ - 3] = (1 << b_) - 1
-        assert pop(O.pack_v_codes_tiled(one, b_)) == b_
-
-
-def test_pack_meta_positions_and_pairing():
-    """K/V metadata layouts (include/vc.h): hand-derived positions, and the
-    property the K layout exists for -- each dword of a plane pairs the two
-    channels that one packed K code dword carries at bits b and b + 16."""
-    def kpos(D, bits, c):
-        s = np.zeros((1, D), np.float16)
-        s[0, c] = 1.0
-        out = O.pack_k_meta(s, np.zeros_like(s), bits)
-        nz = np.nonzero(out[0, 0])[0]
-        assert len(nz) == 1 and not out[0, 1].any()
-        return int(nz[0])
-    # int2, D 128: channel 0 -> 0; 8 -> h 1 -> 1; 1 -> pi 1 -> 2; 16 -> d 1, pi 8 -> ks 2 -> 16; 32 -> quad 1 -> 32
-    assert [kpos(128, 2, c) for c in (0, 8, 1, 16, 32)] == [0, 1, 2, 16, 32]
-    # int4, D 128: channel 4 -> h 1 -> 1; 9 -> d 1, j 1 -> pi 5 -> ks 1, i 1 -> 2 (4 + 1) = 10
-    assert [kpos(128, 4, c) for c in (4, 9)] == [1, 10]
-    for D, bits in [(64, 2), (64, 4), (128, 2), (128, 4)]:
-        per = 8 // bits
-        pos = [kpos(D, bits, c) for c in range(D)]
-        assert sorted(pos) == list(range(D))
-        for c1 in range(D):
-            c2 = pos.index(pos[c1] ^ 1)
-            if pos[c1] % 2:
-                continue
-            # bit of channel c in a packed code row (pack_codes): byte c // per, bit bits (c % per)
-            b1 = 8 * (c1 // per) + bits * (c1 % per)
-            b2 = 8 * (c2 // per) + bits * (c2 % per)
-            assert b1 // 32 == b2 // 32 and b2 % 32 == b1 % 32 + 16, (D, bits, c1, c2)
-    # V: token tau -> slot 8 ((tau % 16) // 4) + tau % 4 + 4 (tau // 16); groups keep their order
-    n, G = 64, 4
-    s = np.arange(n * G, dtype=np.float16).reshape(n, G)
-    out = O.pack_v_meta(s, -s)
-    assert out[0, 0, 0, 0] == s[0, 0].view(np.uint16)
-    assert out[0, 0, 4, 0] == s[16, 0].view(np.uint16)        # tau 16 -> slot 4
-    assert out[0, 2, 8 + 1, 0] == s[5, 2].view(np.uint16)     # tau 5 -> slot 9
-    assert out[1, 3, 8 * 3 + 4 + 3, 1] == (-s[32 + 31, 3]).view(np.uint16)  # tau 31 -> slot 31
-    assert sorted(out[..., 0].reshape(-1).tolist()) == sorted(s.view(np.uint16).reshape(-1).tolist())
-
-
 def test_dequant_fraction_exact():
     rng = np.random.default_rng(2)
     codes = rng.integers(0, 16, (64, 64)).astype(np.uint8)
@@ -234,6 +162,103 @@ def test_dequant_fraction_exact():
     for (t, c) in [(0, 0), (31, 63), (32, 1), (63, 17)]:
         exact = int(codes[t, c]) * Fraction(float(s[t // 32, c])) + Fraction(float(z[t // 32, c]))
         assert d[t, c] == float(np.float32(float(exact)))
+
+
+def pin_dequant_v(dequant_v):
+    """V dequantisation against exact fractions: value (t, c) takes the fp16 pair
+    of group c // 32 of its own token t, and code * s + z is rounded once to
+    fp32.  The scales carry a full 11-bit significand, so for most codes the
+    exact value needs more than 11 bits: an fp16 rounding of the result, or of
+    the product alone, shows; a pair taken from another group or token shows."""
+    n, D = 3, 96
+    codes = (np.arange(n * D).reshape(n, D) * 7 % 16).astype(np.uint8)
+    s = np.array([[1 + 2 ** -10, 0.3330078125, 3.0009765625],
+                  [0.0999755859375, 1.2001953125, 0.0],
+                  [5.00390625, 2 ** -14 * 1.5, 0.7001953125]], np.float16)
+    z = np.array([[-1.0009765625, 0.5, -7.25],
+                  [2.001953125, -0.0999755859375, 1.5],
+                  [-3.0, 0.0, 6.00390625]], np.float16)
+    d = dequant_v(codes, s, z)
+    assert d.shape == (n, D)
+    for t in range(n):
+        for c in range(D):
+            exact = int(codes[t, c]) * Fraction(float(s[t, c // 32])) + Fraction(float(z[t, c // 32]))
+            assert d[t, c] == float(np.float32(float(exact))), (t, c)
+    # hand values: t 0, c 1 (code 7, group 0): 7 (1 + 2^-10) - 1.0009765625 = 6 + 7 2^-10 - 2^-10 = 6.005859375
+    assert d[0, 1] == 6.005859375
+    # t 1, c 70 (code (96 + 70) 7 % 16 = 10, group 2, s = 0): exactly the zero point 1.5
+    assert d[1, 70] == 1.5
+
+
+def test_dequant_v_pin():
+    pin_dequant_v(O.dequant_v)
+
+
+def pin_logits(logits):
+    """Logits of one position: the head outputs concatenated head by head, then
+    times W.  A 2-head, 2-channel example worked by hand, where the head-major
+    order is visible, and a random one against the sum over heads of each
+    head's output times its own D rows of W (a block decomposition of the same
+    product)."""
+    o = np.array([[1.0, 2.0], [3.0, 4.0]])
+    W = np.array([[1.0, 0.0, 0.0], [0.0, 1.0, 0.0], [0.0, 0.0, 1.0], [1.0, 1.0, 1.0]])
+    # concat = [1, 2, 3, 4]: column v is x_v + 4
+    assert list(logits(o, W)) == [5.0, 6.0, 7.0]
+    rng = np.random.default_rng(23)
+    Hq, D, V = 3, 4, 5
+    o = rng.standard_normal((Hq, D))
+    W = rng.standard_normal((Hq * D, V))
+    want = sum(o[h] @ W[h * D:(h + 1) * D] for h in range(Hq))
+    got = logits(o, W)
+    assert got.shape == (V,)
+    assert np.allclose(got, want, atol=1e-13, rtol=0)
+
+
+def test_logits_pin():
+    pin_logits(O.logits)
+
+
+def test_dequant_v_and_logits_pins_catch_planted_mistakes():
+    def dv_swapped(codes, s, z):
+        return O.dequant_v(codes, z, s)
+
+    def dv_f16_round(codes, s, z):
+        sf = np.repeat(O.f16_to_f64(s), 32, axis=1)
+        zf = np.repeat(O.f16_to_f64(z), 32, axis=1)
+        return (codes * sf + zf).astype(np.float16).astype(np.float64)
+
+    def dv_f16_product(codes, s, z):
+        sf = np.repeat(O.f16_to_f64(s), 32, axis=1)
+        zf = np.repeat(O.f16_to_f64(z), 32, axis=1)
+        return O.f64_to_f32_rn((codes * sf).astype(np.float16).astype(np.float64) + zf)
+
+    def dv_interleaved_groups(codes, s, z):
+        # channel c in group c % (D/32) instead of c // 32
+        sf = np.tile(O.f16_to_f64(s), (1, 32))
+        zf = np.tile(O.f16_to_f64(z), (1, 32))
+        return O.f64_to_f32_rn(codes * sf + zf)
+
+    def dv_first_token_pairs(codes, s, z):
+        # every token reads the pairs of token 0 (a group per channel range, not per token)
+        return O.dequant_v(codes, np.repeat(s[:1], len(s), 0), np.repeat(z[:1], len(z), 0))
+
+    for bad in (dv_swapped, dv_f16_round, dv_f16_product, dv_interleaved_groups, dv_first_token_pairs):
+        with pytest.raises(AssertionError):
+            pin_dequant_v(bad)
+
+    def lg_channel_major(o, W):
+        return o.T.reshape(-1) @ W
+
+    def lg_heads_reversed(o, W):
+        return o[::-1].reshape(-1) @ W
+
+    def lg_mean_of_heads(o, W):
+        D = o.shape[1]
+        return sum(o[h] @ W[h * D:(h + 1) * D] for h in range(o.shape[0])) / o.shape[0]
+
+    for bad in (lg_channel_major, lg_heads_reversed, lg_mean_of_heads):
+        with pytest.raises(AssertionError):
+            pin_logits(bad)
 
 
 # -------------------------------------------------------------- attention ---

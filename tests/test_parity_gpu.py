@@ -100,25 +100,98 @@ def test_quantize_bit_exact(D, bits):
     from compressed_kv_draft_amd.workload import bf16_dev
     kd, vd = bf16_dev(K, "cuda"), bf16_dev(V, "cuda")
     comp = vc.quantize_kv(kd, vd, bits, nq)
-    torch.cuda.synchronize()
-    kc = comp.t["k_codes"].cpu().numpy()
-    vcd = comp.t["v_codes"].cpu().numpy()
-    km = comp.t["k_meta"].cpu().numpy()
-    vm = comp.t["v_meta"].cpu().numpy()
+    kc, vcd, km, vm = (t.cpu().numpy() for t in vc.unpack_quant(comp, w.B, w.Hkv, D))
     for b in range(w.B):
         for h in range(w.Hkv):
             kf = O.bf16_to_f64(K[b, h, :nq]).astype(np.float32)
             vf = O.bf16_to_f64(V[b, h, :nq]).astype(np.float32)
+            _check_canonical_unit(kc[b, h], km[b, h], vcd[b, h], vm[b, h], kf, vf, bits, (b, h))
             c, s, z = O.quantize_k(kf, bits)
-            assert np.array_equal(kc[b, h], O.pack_codes(c, bits)), (b, h, "k codes")
-            assert np.array_equal(km[b, h].view(np.uint16), O.pack_k_meta(s, z, bits)), (b, h, "k meta")
             dq = vc.debug_dequant(comp, w.B, w.Hkv, D, b, h, 0).cpu().numpy()
             assert np.array_equal(dq.astype(np.float64), O.dequant_k(c, s, z)), (b, h, "k dequant")
             c, s, z = O.quantize_v(vf, bits)
-            assert np.array_equal(vcd[b, h].reshape(-1), O.pack_v_codes_tiled(c, bits)), (b, h, "v codes")
-            assert np.array_equal(vm[b, h].view(np.uint16), O.pack_v_meta(s, z)), (b, h, "v meta")
             dq = vc.debug_dequant(comp, w.B, w.Hkv, D, b, h, 1).cpu().numpy()
             assert np.array_equal(dq.astype(np.float64), O.dequant_v(c, s, z)), (b, h, "v dequant")
+
+
+def _canonical(kf, vf, bits):
+    """The oracle's quantisation of one unit in the canonical form of the C header:
+    packed K and V code rows, K pairs [n/32, D, 2] and V pairs [n, D/32, 2] as f16 bits."""
+    c, s, z = O.quantize_k(kf, bits)
+    cv, sv, zv = O.quantize_v(vf, bits)
+    pair = lambda a, b: np.stack([a.view(np.uint16), b.view(np.uint16)], axis=-1)
+    return O.pack_codes(c, bits), pair(s, z), O.pack_codes(cv, bits), pair(sv, zv)
+
+
+def _check_canonical_unit(kc, km, vcd, vm, kf, vf, bits, where):
+    ck, ckm, cv, cvm = _canonical(kf, vf, bits)
+    assert np.array_equal(kc, ck), (where, "k codes")
+    assert np.array_equal(km.view(np.uint16), ckm), (where, "k meta")
+    assert np.array_equal(vcd, cv), (where, "v codes")
+    assert np.array_equal(vm.view(np.uint16), cvm), (where, "v meta")
+
+
+@pytest.mark.parametrize("D,bits", QUANT_CASES)
+def test_pack_canonical_feeds_draft(D, bits):
+    """A compressor outside the library hands over the canonical form (here the
+    oracle's own quantisation): vc_pack_quant turns it into the cache
+    vc_draft_attn reads.  The packed cache equals vc_quantize_kv's byte for
+    byte, unpacks to the same canonical arrays, and drafts like the oracle."""
+    import torch
+    vc = _vc()
+    from compressed_kv_draft_amd.workload import bf16_dev
+    print(f"[case] pack canonical D={D} bits={bits}", flush=True)
+    w = C.TINY.with_(B=2, Hkv=2, Hq=8, D=D, L=384, seed=71 + D + bits)
+    K = I.context_kv(w, "k")
+    V = I.context_kv(w, "v")
+    n, R = 320, 40
+    canon = [np.zeros((w.B, w.Hkv) + shape, np.uint16 if i % 2 else np.uint8) for i, shape in
+             enumerate([(n, D * bits // 8), (n // 32, D, 2), (n, D * bits // 8), (n, D // 32, 2)])]
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            kf = O.bf16_to_f64(K[b, h, :n]).astype(np.float32)
+            vf = O.bf16_to_f64(V[b, h, :n]).astype(np.float32)
+            for arr, part in zip(canon, _canonical(kf, vf, bits)):
+                arr[b, h] = part
+    dev = [torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda() for a in canon]
+    kc_d, km_d, vc_d, vm_d = dev[0], dev[1].view(torch.float16), dev[2], dev[3].view(torch.float16)
+    comp = vc.empty_quant(w.B, w.Hkv, D, bits, n + 64, "cuda")
+    # two appends (blocks 0..5, then 6..9) to exercise dst_block
+    vc.pack_quant(kc_d[:, :, :192].contiguous(), vc_d[:, :, :192].contiguous(), km_d[:, :, :6].contiguous(),
+                  vm_d[:, :, :192].contiguous(), comp)
+    vc.pack_quant(kc_d[:, :, 192:].contiguous(), vc_d[:, :, 192:].contiguous(), km_d[:, :, 6:].contiguous(),
+                  vm_d[:, :, 192:].contiguous(), comp)
+    assert comp.desc.n_quant == n
+    ref = vc.quantize_kv(bf16_dev(K, "cuda"), bf16_dev(V, "cuda"), bits, n, capacity=n + 64)
+    torch.cuda.synchronize()
+    for f in ("k_codes", "v_codes", "k_meta", "v_meta"):
+        a = comp.t[f].view(torch.uint8).reshape(w.B, w.Hkv, -1)
+        r = ref.t[f].view(torch.uint8).reshape(w.B, w.Hkv, -1)
+        live = a.shape[2] * n // (n + 64)
+        assert torch.equal(a[:, :, :live], r[:, :, :live]), f
+    kc, vcd, km, vm = (t.cpu().numpy() for t in vc.unpack_quant(comp, w.B, w.Hkv, D))
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            assert np.array_equal(kc[b, h], canon[0][b, h]) and np.array_equal(vcd[b, h], canon[2][b, h])
+            assert np.array_equal(km[b, h].view(np.uint16), canon[1][b, h])
+            assert np.array_equal(vm[b, h].view(np.uint16), canon[3][b, h])
+    tk = bf16_dev(np.ascontiguousarray(K[:, :, n:n + R]), "cuda")
+    tv = bf16_dev(np.ascontiguousarray(V[:, :, n:n + R]), "cuda")
+    tail = vc.Tail(tk, tv, torch.full((w.B,), R, dtype=torch.int32, device="cuda"))
+    Q = I.queries(w)[:, :, 0]
+    scale = O.scale_for(D)
+    got = vc.draft_attn(comp, tail, bf16_dev(np.ascontiguousarray(Q), "cuda"), scale).cpu().numpy()
+    g = w.Hq // w.Hkv
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            kf = O.bf16_to_f64(K[b, h, :n]).astype(np.float32)
+            vf = O.bf16_to_f64(V[b, h, :n]).astype(np.float32)
+            keys, vals = O.draft_kv_rows("quant", k_deq=O.dequant_k(*O.quantize_k(kf, bits)),
+                                         v_deq=O.dequant_v(*O.quantize_v(vf, bits)),
+                                         tail_k=O.bf16_to_f64(K[b, h, n:n + R]),
+                                         tail_v=O.bf16_to_f64(V[b, h, n:n + R]))
+            want = O.draft_attention_unit(O.bf16_to_f64(Q[b, h * g:(h + 1) * g]), keys, vals, scale)
+            assert_close(got[b, h * g:(h + 1) * g], want, f"packed draft D{D} int{bits} b{b} h{h}")
 
 
 ROLLOVER_CASES = [(64, 4), (128, 2), (128, 4)]
@@ -156,24 +229,20 @@ def test_quantize_rollover_blocks(D, bits):
         n += 32 * nb
     assert n == comp.t["n_quant"] == comp.desc.n_quant == 352
     torch.cuda.synchronize()
-    kc = comp.t["k_codes"].cpu().numpy()
-    vcd = comp.t["v_codes"].cpu().numpy()
-    km = comp.t["k_meta"].cpu().numpy()
-    vm = comp.t["v_meta"].cpu().numpy()
+    raw = {f: comp.t[f].view(torch.uint8).reshape(w.B, w.Hkv, -1).cpu().numpy()
+           for f in ("k_codes", "v_codes", "k_meta", "v_meta")}
+    kc, vcd, km, vm = (t.cpu().numpy() for t in vc.unpack_quant(comp, w.B, w.Hkv, D))
     for b in range(w.B):
         for h in range(w.Hkv):
             kf = O.bf16_to_f64(K[b, h, :n]).astype(np.float32)
             vf = O.bf16_to_f64(V[b, h, :n]).astype(np.float32)
+            _check_canonical_unit(kc[b, h], km[b, h], vcd[b, h], vm[b, h], kf, vf, bits, (b, h))
             c, s, z = O.quantize_k(kf, bits)
-            assert np.array_equal(kc[b, h, :n], O.pack_codes(c, bits)), (b, h, "k codes")
-            assert np.array_equal(km[b, h, :n // 32].view(np.uint16), O.pack_k_meta(s, z, bits)), (b, h, "k meta")
             dq = vc.debug_dequant(comp, w.B, w.Hkv, D, b, h, 0).cpu().numpy()
             assert np.array_equal(dq.astype(np.float64), O.dequant_k(c, s, z)), (b, h, "k dequant")
-            c, s, z = O.quantize_v(vf, bits)
-            assert np.array_equal(vcd[b, h, :n].reshape(-1), O.pack_v_codes_tiled(c, bits)), (b, h, "v codes")
-            assert np.array_equal(vm[b, h, :n // 32].view(np.uint16), O.pack_v_meta(s, z)), (b, h, "v meta")
-            for arr, nb_rows in ((kc, n), (vcd, n), (km, n // 32), (vm, n // 32)):
-                assert (arr[b, h, nb_rows:].view(np.uint8) == 0xA5).all(), (b, h, "past n_quant")
+            for f, arr in raw.items():
+                live = arr.shape[2] * n // cap
+                assert (arr[b, h, live:] == 0xA5).all(), (b, h, f, "past n_quant")
     # draft over the grown cache: quantised [0, n), then exact rows [n, n + R)
     tk = bf16_dev(np.ascontiguousarray(K[:, :, n:n + R]), "cuda")
     tv = bf16_dev(np.ascontiguousarray(V[:, :, n:n + R]), "cuda")
@@ -316,6 +385,12 @@ CHUNK_CASES = [
     (C.TINY.with_(name="chunk_paged_d128_g8", B=2, Hq=16, Hkv=2, D=128, L=1200, k=32, paged=True, page_tokens=16,
                   seed=45), [256, 512, 768, 1024]),
     (C.TINY.with_(name="chunk_d64_g4_k3", B=3, Hq=8, Hkv=2, D=64, L=97, k=3, seed=46), [40]),
+    # paged ranges that start inside a page, at rows that are not multiples of
+    # 8: a load instruction must not read rows of the next page from this one
+    (C.TINY.with_(name="chunk_paged_d64_unaligned", B=2, Hq=8, Hkv=2, D=64, L=1204, k=7, paged=True,
+                  page_tokens=16, seed=47), [203, 700]),
+    (C.TINY.with_(name="chunk_paged_d128_g8_unaligned", B=2, Hq=16, Hkv=2, D=128, L=1203, k=32, paged=True,
+                  page_tokens=8, seed=48), [5, 299, 1195]),
 ]
 
 
@@ -698,7 +773,30 @@ def _random_cases(n=14, seed=2026):
     return out
 
 
-@pytest.mark.parametrize("w", _random_cases(), ids=lambda w: w.name)
+def _odd_group_cases():
+    """GQA groups that are not powers of two (3, 5, 6, 7): the draft's replica
+    count 8 // g leaves idle column slots, and at D = 128 with g >= 5 every
+    lane carries two V channel groups."""
+    out = []
+    specs = [("quant2", 64, 3), ("quant4", 128, 3), ("token_drop", 128, 3), ("identity", 64, 5),
+             ("quant2", 128, 5), ("quant4", 64, 6), ("quant2", 128, 6), ("token_drop", 64, 6),
+             ("quant4", 128, 7), ("identity", 128, 7)]
+    for i, (kind, D, g) in enumerate(specs):
+        Hkv = 1 + i % 3
+        L = 300 + 173 * i
+        kw = dict(name=f"oddg{i}_{kind}_d{D}_g{g}_kv{Hkv}_l{L}", B=1 + i % 2, Hq=g * Hkv, Hkv=Hkv, D=D, L=L,
+                  k=3, seed=300 + i)
+        if kind.startswith("quant"):
+            kw.update(kind="quant", bits=int(kind[-1]), residual=L % 32 + 32)
+        elif kind == "token_drop":
+            kw.update(kind="token_drop", keep_frac=0.25)
+        else:
+            kw.update(kind="identity")
+        out.append(C.TINY.with_(**kw))
+    return out
+
+
+@pytest.mark.parametrize("w", _random_cases() + _odd_group_cases(), ids=lambda w: w.name)
 def test_random_shapes_draft_and_verify(w):
     from compressed_kv_draft_amd.workload import DeviceWorkload
     print(f"[case] random {w.name}", flush=True)
