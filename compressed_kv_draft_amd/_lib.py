@@ -58,6 +58,8 @@ EXPORTS = {
     "vc_draft_ws_bytes": (c_size, [c_int, c_int, c_int, c_int, c_int]),
     "vc_draft_attn": (c_int, [ctypes.POINTER(VcKvComp), ctypes.POINTER(VcTail), c_void, c_void, c_void,
                               c_int, c_int, c_int, c_int, c_float, c_void, c_size, c_void]),
+    "vc_draft_attn_noalloc": (c_int, [ctypes.POINTER(VcKvComp), ctypes.POINTER(VcTail), c_void, c_void, c_void,
+                                      c_int, c_int, c_int, c_int, c_float, c_void]),
     "vc_verify_ws_bytes": (c_size, [c_int, c_int, c_int, c_int, c_int, c_int]),
     "vc_verify_attn": (c_int, [c_void, ctypes.POINTER(VcKvFull), c_void, c_int, c_int, c_void,
                                c_int, c_int, c_int, c_int, c_float, c_void, c_size, c_void]),
@@ -312,6 +314,20 @@ def draft_attn(comp: Compressed, tail: Tail, q: torch.Tensor, scale: float, out=
     rc = LIB.vc_draft_attn(ctypes.byref(comp.desc), ctypes.byref(tail.desc), _ptr(q), _ptr(out), _ptr(lse),
                            B, Hq, Hkv, D, float(scale), _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, "vc_draft_attn")
+    return out
+
+
+def draft_attn_noalloc(comp: Compressed, tail: Tail, q: torch.Tensor, scale: float, out: torch.Tensor,
+                       lse=None, Hkv: int | None = None, stream=None):
+    """vc_draft_attn_noalloc: like draft_attn, but the caller passes `out` and the split
+    partials live in the library's per-GPU scratch array (nothing is allocated)."""
+    B, Hq, D = q.shape
+    if Hkv is None:
+        ref = comp.t.get("k_codes") if comp.kind == "quant" else comp.t.get("k_full")
+        Hkv = ref.shape[1]
+    rc = LIB.vc_draft_attn_noalloc(ctypes.byref(comp.desc), ctypes.byref(tail.desc), _ptr(q), _ptr(out), _ptr(lse),
+                                   B, Hq, Hkv, D, float(scale), _stream(stream))
+    _check(rc, "vc_draft_attn_noalloc")
     return out
 
 

@@ -835,15 +835,18 @@ extern "C" size_t vc_draft_ws_bytes(int B, int Hq, int Hkv, int D, int max_keys)
   return draft_ws_need(B, Hq, Hkv, D, s);
 }
 
-extern "C" int vc_draft_attn(const vc_kv_comp* comp, const vc_tail* tail, const void* q, float* out,
-                             float* lse, int B, int Hq, int Hkv, int D, float scale, void* ws,
-                             size_t ws_bytes, hipStream_t stream) {
-  VC_CHECK(comp != nullptr && q != nullptr && out != nullptr, "vc_draft_attn: null comp/q/out");
-  VC_CHECK(B > 0 && Hq > 0 && Hkv > 0 && Hq % Hkv == 0, "vc_draft_attn: bad B/Hq/Hkv (%d,%d,%d)", B, Hq, Hkv);
-  if (D != 64 && D != 128) return fail(VC_ERR_UNSUPPORTED, "vc_draft_attn: D=%d not in {64,128}", D);
+// Validates, plans and launches one draft step.  ws/ws_bytes: the split
+// partials' buffer (caller's workspace, or the file-scope scratch array for
+// the allocation-free entry point, which reports its own limit).
+static int draft_launch(const char* fn, bool scratch_ws, const vc_kv_comp* comp, const vc_tail* tail,
+                        const void* q, float* out, float* lse, int B, int Hq, int Hkv, int D, float scale,
+                        void* ws, size_t ws_bytes, hipStream_t stream) {
+  VC_CHECK(comp != nullptr && q != nullptr && out != nullptr, "%s: null comp/q/out", fn);
+  VC_CHECK(B > 0 && Hq > 0 && Hkv > 0 && Hq % Hkv == 0, "%s: bad B/Hq/Hkv (%d,%d,%d)", fn, B, Hq, Hkv);
+  if (D != 64 && D != 128) return fail(VC_ERR_UNSUPPORTED, "%s: D=%d not in {64,128}", fn, D);
   const int g = Hq / Hkv;
-  if (g > 8) return fail(VC_ERR_UNSUPPORTED, "vc_draft_attn: GQA group %d > 8", g);
-  VC_CHECK(aligned(q, 16) && aligned(out, 16), "vc_draft_attn: q/out must be 16-byte aligned");
+  if (g > 8) return fail(VC_ERR_UNSUPPORTED, "%s: GQA group %d > 8", fn, g);
+  VC_CHECK(aligned(q, 16) && aligned(out, 16), "%s: q/out must be 16-byte aligned", fn);
   DraftArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.out = out;
@@ -856,16 +859,16 @@ extern "C" int vc_draft_attn(const vc_kv_comp* comp, const vc_tail* tail, const 
   int bits = 0;
   switch (comp->kind) {
     case VC_KV_QUANT:
-      VC_CHECK(comp->bits == 2 || comp->bits == 4, "vc_draft_attn: bits must be 2 or 4 (got %d)", comp->bits);
-      VC_CHECK(comp->n_quant >= 0 && comp->n_quant % 32 == 0, "vc_draft_attn: n_quant=%d not a multiple of 32",
+      VC_CHECK(comp->bits == 2 || comp->bits == 4, "%s: bits must be 2 or 4 (got %d)", fn, comp->bits);
+      VC_CHECK(comp->n_quant >= 0 && comp->n_quant % 32 == 0, "%s: n_quant=%d not a multiple of 32", fn,
                comp->n_quant);
       VC_CHECK(comp->n_quant == 0 || (comp->k_codes && comp->v_codes && comp->k_meta && comp->v_meta),
-               "vc_draft_attn: null codes/meta");
+               "%s: null codes/meta", fn);
       VC_CHECK(aligned(comp->k_codes, 16) && aligned(comp->v_codes, 16) && aligned(comp->k_meta, 16) &&
                    aligned(comp->v_meta, 16),
-               "vc_draft_attn: codes and meta must be 16-byte aligned");
+               "%s: codes and meta must be 16-byte aligned", fn);
       VC_CHECK(quant_cap(comp) >= comp->n_quant && quant_cap(comp) % 32 == 0,
-               "vc_draft_attn: q_cap=%d below n_quant=%d or not a multiple of 32", comp->q_cap, comp->n_quant);
+               "%s: q_cap=%d below n_quant=%d or not a multiple of 32", fn, comp->q_cap, comp->n_quant);
       bits = comp->bits;
       a.q_cap = quant_cap(comp);
       a.n_main = comp->n_quant;
@@ -876,37 +879,37 @@ extern "C" int vc_draft_attn(const vc_kv_comp* comp, const vc_tail* tail, const 
       break;
     case VC_KV_IDENTITY:
     case VC_KV_TOKEN_DROP:
-      VC_CHECK(comp->L_cap >= 0, "vc_draft_attn: bad L_cap");
-      VC_CHECK(comp->L_full >= 0 && comp->L_full <= comp->L_cap, "vc_draft_attn: L_full=%d outside [0, L_cap=%d]",
+      VC_CHECK(comp->L_cap >= 0, "%s: bad L_cap", fn);
+      VC_CHECK(comp->L_full >= 0 && comp->L_full <= comp->L_cap, "%s: L_full=%d outside [0, L_cap=%d]", fn,
                comp->L_full, comp->L_cap);
       if (comp->kind == VC_KV_IDENTITY) {
         a.n_main = comp->L_full;
         a.keep_idx = nullptr;
       } else {
-        VC_CHECK(comp->n_keep >= 0, "vc_draft_attn: bad n_keep");
-        VC_CHECK(comp->n_keep == 0 || comp->keep_idx != nullptr, "vc_draft_attn: null keep_idx");
+        VC_CHECK(comp->n_keep >= 0, "%s: bad n_keep", fn);
+        VC_CHECK(comp->n_keep == 0 || comp->keep_idx != nullptr, "%s: null keep_idx", fn);
         a.n_main = comp->n_keep;
         a.keep_idx = comp->keep_idx;
       }
-      VC_CHECK(a.n_main == 0 || (comp->k_full && comp->v_full), "vc_draft_attn: null k_full/v_full");
-      VC_CHECK(aligned(comp->k_full, 16) && aligned(comp->v_full, 16), "vc_draft_attn: k_full/v_full misaligned");
+      VC_CHECK(a.n_main == 0 || (comp->k_full && comp->v_full), "%s: null k_full/v_full", fn);
+      VC_CHECK(aligned(comp->k_full, 16) && aligned(comp->v_full, 16), "%s: k_full/v_full misaligned", fn);
       a.k_full = static_cast<const uint16_t*>(comp->k_full);
       a.v_full = static_cast<const uint16_t*>(comp->v_full);
       a.L_cap = comp->L_cap;
       a.row_bound = comp->L_full;
       break;
     default:
-      return fail(VC_ERR_INVALID, "vc_draft_attn: unknown compressor kind %d", comp->kind);
+      return fail(VC_ERR_INVALID, "%s: unknown compressor kind %d", fn, comp->kind);
   }
   if (tail != nullptr && tail->T_cap > 0) {
-    VC_CHECK(tail->k && tail->v && tail->len, "vc_draft_attn: null tail pointers");
-    VC_CHECK(aligned(tail->k, 16) && aligned(tail->v, 16), "vc_draft_attn: tail misaligned");
+    VC_CHECK(tail->k && tail->v && tail->len, "%s: null tail pointers", fn);
+    VC_CHECK(aligned(tail->k, 16) && aligned(tail->v, 16), "%s: tail misaligned", fn);
     a.tail_k = static_cast<const uint16_t*>(tail->k);
     a.tail_v = static_cast<const uint16_t*>(tail->v);
     a.tail_len = tail->len;
     a.T_cap = tail->T_cap;
   } else {
-    VC_CHECK(tail == nullptr || tail->T_cap == 0, "vc_draft_attn: negative T_cap");
+    VC_CHECK(tail == nullptr || tail->T_cap == 0, "%s: negative T_cap", fn);
     a.T_cap = 0;
   }
   const int units = B * Hkv;
@@ -918,12 +921,15 @@ extern "C" int vc_draft_attn(const vc_kv_comp* comp, const vc_tail* tail, const 
   const DraftKernel kern = D == 128 ? (nv == 2 ? pick_kernel<128, 2>(bits) : pick_kernel<128, 1>(bits))
                                     : pick_kernel<64, 1>(bits);
   const DraftPlan p = plan_draft(units, main_blocks, tail_blocks, wgs_per_cu(kern), bits);
-  VC_CHECK(p.splits <= kMaxCombineSplits, "vc_draft_attn: %d splits exceed %d", p.splits, kMaxCombineSplits);
+  VC_CHECK(p.splits <= kMaxCombineSplits, "%s: %d splits exceed %d", fn, p.splits, kMaxCombineSplits);
   const size_t need = draft_ws_need(B, Hq, Hkv, D, p.splits);
   if (p.splits > 1) {
+    if (scratch_ws && need > ws_bytes)
+      return fail(VC_ERR_UNSUPPORTED, "%s: this call needs %zu bytes of split partials, above the %zu-byte "
+                  "scratch array (use vc_draft_attn with a workspace)", fn, need, ws_bytes);
     if (ws == nullptr || ws_bytes < need)
-      return fail(VC_ERR_WORKSPACE, "vc_draft_attn: workspace %zu < %zu bytes", ws_bytes, need);
-    VC_CHECK(aligned(ws, 16), "vc_draft_attn: workspace misaligned");
+      return fail(VC_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+    VC_CHECK(aligned(ws, 16), "%s: workspace misaligned", fn);
     a.ws = static_cast<float*>(ws);
   }
   a.main_splits = p.main_splits;
@@ -935,7 +941,7 @@ extern "C" int vc_draft_attn(const vc_kv_comp* comp, const vc_tail* tail, const 
   a.direct = p.splits == 1;
   a.xcd_affine = units % 8 == 0 ? 1 : 0;
   if (a.xcd_affine) {
-    VC_CHECK((long long)p.main_splits * units < (1LL << 31), "vc_draft_attn: grid too large");
+    VC_CHECK((long long)p.main_splits * units < (1LL << 31), "%s: grid too large", fn);
     kern<<<dim3(p.main_splits * units), kThreads, 0, stream>>>(a);
   } else {
     kern<<<dim3(p.main_splits, units), kThreads, 0, stream>>>(a);
@@ -946,4 +952,46 @@ extern "C" int vc_draft_attn(const vc_kv_comp* comp, const vc_tail* tail, const 
     VC_HIP(hipGetLastError());
   }
   return VC_OK;
+}
+
+extern "C" int vc_draft_attn(const vc_kv_comp* comp, const vc_tail* tail, const void* q, float* out,
+                             float* lse, int B, int Hq, int Hkv, int D, float scale, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  return draft_launch("vc_draft_attn", false, comp, tail, q, out, lse, B, Hq, Hkv, D, scale, ws, ws_bytes, stream);
+}
+
+// ------------------------------------------------------------------------
+// Allocation-free draft: the split partials live in a file-scope device array
+// (one copy per GPU, held until the process ends).  In host code `scratch`
+// names a host-side stand-in, never the device copy: its device address is
+// taken once per device with hipGetSymbolAddress and only that address is
+// handed to kernels.  The partials need no clearing: every slot a combine
+// reads is written by the same call first.
+constexpr size_t kScratchBytes = VC_DRAFT_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+static int scratch_ptr(void** out) {
+  static std::mutex mu;
+  static std::map<int, void*> ptrs;
+  int dev = 0;
+  VC_HIP(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = ptrs.find(dev);
+  if (it == ptrs.end()) {
+    void* p = nullptr;
+    VC_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    VC_CHECK(p != nullptr && aligned(p, 256), "vc_draft_attn_noalloc: scratch array has no usable device address");
+    it = ptrs.emplace(dev, p).first;
+  }
+  *out = it->second;
+  return VC_OK;
+}
+
+extern "C" int vc_draft_attn_noalloc(const vc_kv_comp* comp, const vc_tail* tail, const void* q, float* out,
+                                     float* lse, int B, int Hq, int Hkv, int D, float scale, hipStream_t stream) {
+  void* ws = nullptr;
+  const int rc = scratch_ptr(&ws);
+  if (rc != VC_OK) return rc;
+  return draft_launch("vc_draft_attn_noalloc", true, comp, tail, q, out, lse, B, Hq, Hkv, D, scale, ws,
+                      kScratchBytes, stream);
 }

@@ -270,6 +270,22 @@ int vc_draft_attn(const vc_kv_comp* comp, const vc_tail* tail, const void* q, fl
                   size_t ws_bytes, hipStream_t stream);
 
 /*
+ * vc_draft_attn_noalloc — vc_draft_attn for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace.  The split partials
+ * go to a scratch array of VC_DRAFT_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on until the process ends; the call itself allocates
+ * nothing.  Every call on one GPU shares that GPU's array, so calls that
+ * overlap in time on one GPU (different streams, or several threads) race
+ * and must be ordered by the caller.  A call whose partials would not fit
+ * (vc_draft_ws_bytes gives an upper bound) returns VC_ERR_UNSUPPORTED before
+ * enqueueing anything.  Results are identical to vc_draft_attn's.
+ */
+#define VC_DRAFT_SCRATCH_BYTES (16u << 20)
+int vc_draft_attn_noalloc(const vc_kv_comp* comp, const vc_tail* tail, const void* q, float* out, float* lse,
+                          int B, int Hq, int Hkv, int D, float scale, hipStream_t stream);
+
+/*
  * vc_verify_attn — causal verification of n_q positions in one pass.
  * [VC Core Algorithm: a single forward pass with KV_full verifies all drafted
  * tokens in parallel; VC Key System Innovations P1: verification is
