@@ -179,3 +179,118 @@ def verify_flops(w: Workload) -> int:
     """q.k and p.v MACs x 2 over the causal key ranges."""
     keys = sum(w.L + j + 1 for j in range(w.n_q))
     return 2 * 2 * w.B * w.Hq * keys * w.D
+
+
+class CycleWorkload:
+    """Device and host state of the staggered two-group cycle (harness glue).
+
+    The batch is split into request groups of B / groups sequences.  Each group
+    has its own QUANT draft cache (device, `rotate` copies so that consecutive
+    draft steps read different buffers, as consecutive layers would), exact
+    tail (recent window + the round's drafted rows) and queries.  The full
+    context KV of every sequence lives in one pinned host pool of shuffled
+    pages (the layout of include/vc.h's paged cache).  The device holds one
+    region for the full KV of the group being verified (chunk c of all its
+    sequences after chunk c - 1, as the prefetch lands them) followed by the
+    pages of every group's new rows, which exist only on the device; each
+    group has a device page table into that pool.
+    """
+
+    def __init__(self, w: Workload, device="cuda", rotate: int = 2, with_vocab: bool = True):
+        assert w.kind == "quant" and w.paged and w.L % w.chunk_tokens == 0 and w.chunk_tokens % w.page_tokens == 0
+        self.w = w
+        G = w.groups
+        bg = w.B // G
+        self.bg = bg
+        pt = w.page_tokens
+        table, _ = I.page_table(w)
+        self.table = table                                   # host int32 [B, pages_per_seq]
+        ctx_pages = w.L // pt
+        pps = table.shape[1]
+        extra = pps - ctx_pages
+        self.page_bytes = w.Hkv * 2 * pt * w.D * 2
+        n_ctx_slots = w.B * ctx_pages
+        assert int(table[:, :ctx_pages].max()) < n_ctx_slots
+        self.chunks = [(t, t + w.chunk_tokens) for t in range(0, w.L, w.chunk_tokens)]
+        scp = w.chunk_tokens // pt                           # pages of one sequence in one chunk
+        self.pages_per_chunk = bg * scp
+        self.chunk_bytes = self.pages_per_chunk * self.page_bytes
+        n_region = self.pages_per_chunk * len(self.chunks)
+        self.region_bytes = n_region * self.page_bytes
+        self.host = torch.empty(n_ctx_slots * self.page_bytes, dtype=torch.uint8, pin_memory=True)
+        host_pages = self.host.numpy().view(np.uint16).reshape(n_ctx_slots, w.Hkv, 2, pt, w.D)
+        n_dev_pages = n_region + w.B * extra
+        self.pool = torch.empty(n_dev_pages * self.page_bytes, dtype=torch.uint8, device=device)
+        self.region = self.pool[:self.region_bytes]
+        dev_pages = self.pool.view(torch.int16).view(n_dev_pages, w.Hkv, 2, pt, w.D)
+        Kn, Vn = I.new_rows(w, "k"), I.new_rows(w, "v")
+        Q = I.queries(w)
+        R = w.residual
+        self.seqs, self.comps, self.tails, self.q_steps, self.q_verify, self.full = [], [], [], [], [], []
+        self.np_ctx = {}
+        for gi in range(G):
+            seqs = list(range(gi * bg, (gi + 1) * bg))
+            self.seqs.append(seqs)
+            K = I.context_kv_seqs(w, "k", seqs)
+            V = I.context_kv_seqs(w, "v", seqs)
+            tab = np.empty((bg, pps), dtype=np.int32)
+            for i, b in enumerate(seqs):
+                slots = table[b, :ctx_pages]
+                host_pages[slots, :, 0] = K[i].reshape(w.Hkv, ctx_pages, pt, w.D).transpose(1, 0, 2, 3)
+                host_pages[slots, :, 1] = V[i].reshape(w.Hkv, ctx_pages, pt, w.D).transpose(1, 0, 2, 3)
+                p = np.arange(ctx_pages)
+                tab[i, :ctx_pages] = (p // scp) * self.pages_per_chunk + i * scp + p % scp
+                new_slots = n_region + b * extra + np.arange(extra)
+                tab[i, ctx_pages:] = new_slots
+                pad = extra * pt - w.n_q
+                for which, src in ((0, Kn), (1, Vn)):
+                    rows = np.pad(src[b], ((0, 0), (0, pad), (0, 0))).reshape(w.Hkv, extra, pt, w.D)
+                    dev_pages[torch.from_numpy(new_slots).long().to(device), :, which] = \
+                        torch.from_numpy(np.ascontiguousarray(rows.transpose(1, 0, 2, 3)).view(np.int16)).to(device)
+            # the draft cache: quantise the group's context on the device
+            kd = bf16_dev(K, device)
+            vd = bf16_dev(V, device)
+            comp = vc.quantize_kv(kd, vd, w.bits, w.n_quant)
+            torch.cuda.synchronize()
+            comp.t.pop("src_keepalive", None)
+            self.comps.append([comp] + [clone_compressed(comp) for _ in range(rotate - 1)])
+            del kd, vd
+            tk = np.concatenate([K[:, :, w.L - R:], Kn[seqs]], axis=2)
+            tv = np.concatenate([V[:, :, w.L - R:], Vn[seqs]], axis=2)
+            tkd, tvd = bf16_dev(tk, device), bf16_dev(tv, device)
+            lens = [torch.full((bg,), R + j + 1, dtype=torch.int32, device=device) for j in range(w.k)]
+            self.tails.append([vc.Tail(tkd, tvd, tl) for tl in lens])
+            qv = bf16_dev(Q[seqs], device)
+            self.q_verify.append(qv)
+            self.q_steps.append([qv[:, :, j, :].contiguous() for j in range(w.k)])
+            self.full.append(vc.FullKV(self.pool, None, 0, torch.from_numpy(tab).to(device), pt, pps, n_dev_pages))
+            if gi == 0:
+                self.np_ctx = {"K": K[:2].copy(), "V": V[:2].copy()}   # two sequences for the CPU baseline sample
+            del K, V
+        self.np_q, self.np_kn, self.np_vn = Q, Kn, Vn
+        self.ctx_len = torch.full((bg,), w.L, dtype=torch.int32, device=device)
+        self.scale = float(np.float32(1.0 / np.sqrt(w.D)))
+        self.draft_ws = torch.zeros(vc.draft_ws_bytes(bg, w.Hq, w.Hkv, w.D, w.n_quant + R + w.n_q),
+                                    dtype=torch.uint8, device=device)
+        self.verify_ws = torch.empty(vc.verify_ws_bytes(bg, w.Hq, w.Hkv, w.D, w.n_q, w.L), dtype=torch.uint8,
+                                     device=device)
+        self.draft_out = [torch.empty((w.k, bg, w.Hq, w.D), dtype=torch.float32, device=device) for _ in range(G)]
+        self.verify_out = [torch.empty((bg, w.Hq, w.n_q, w.D), dtype=torch.float32, device=device)
+                           for _ in range(G)]
+        self.W = torch.from_numpy(I.vocab_matrix(w)).to(device) if with_vocab else None
+
+    def draft_step(self, gi: int, j: int, stream=None):
+        w = self.w
+        comps = self.comps[gi]
+        return vc.draft_attn(comps[j % len(comps)], self.tails[gi][j], self.q_steps[gi][j], self.scale,
+                             out=self.draft_out[gi][j], ws=self.draft_ws, Hkv=w.Hkv, stream=stream)
+
+    def draft_logits(self, gi: int):
+        w = self.w
+        o = self.draft_out[gi].permute(1, 0, 2, 3).reshape(self.bg, w.k, w.Hq * w.D)
+        return torch.matmul(o, self.W)
+
+    def verify_logits(self, gi: int):
+        w = self.w
+        o = self.verify_out[gi].permute(0, 2, 1, 3).reshape(self.bg, w.n_q, w.Hq * w.D)
+        return torch.matmul(o, self.W).contiguous()

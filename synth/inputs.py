@@ -29,6 +29,21 @@ def context_kv_unit(w: Workload, which: str, b: int, h: int) -> np.ndarray:
     return f32_to_bf16_bits(normal_f32(w.seed, which, (b, h), (w.L, w.D)))
 
 
+def context_kv_seqs(w: Workload, which: str, seqs) -> np.ndarray:
+    """[len(seqs), Hkv, L, D] rows of ``context_kv`` for the listed sequences only
+    (identical bits; one substream per (b, kv-head), drawn in parallel)."""
+    seqs = [int(b) for b in seqs]
+    out = np.empty((len(seqs), w.Hkv, w.L, w.D), dtype=np.uint16)
+
+    def one(ih):
+        i, h = ih
+        out[i, h] = context_kv_unit(w, which, seqs[i], h)
+
+    with ThreadPoolExecutor(threads_default()) as ex:
+        list(ex.map(one, [(i, h) for i in range(len(seqs)) for h in range(w.Hkv)]))
+    return out
+
+
 def new_rows(w: Workload, which: str) -> np.ndarray:
     assert which in ("k", "v")
     return normal_bf16(w.seed, which + "_new", (w.B, w.Hkv, w.n_q, w.D), unit_dims=2)
