@@ -290,21 +290,25 @@ def calibrate_copy():
           flush=True)
 
 
-def kernel_source_digest():
-    """sha256 of the draft kernel's sources: ties a stored counter reading to the code it was taken on."""
+TRAFFIC_SOURCES = {"draft": ("draft.hip", "lds_dma.h", "mfma.h", "vc_common.h"),
+                   "verify": ("verify.hip", "lds_dma.h", "mfma.h", "vc_common.h")}
+
+
+def kernel_source_digest(kind="draft"):
+    """sha256 of a kernel's sources: ties a stored counter reading to the code it was taken on."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("draft.hip", "lds_dma.h", "mfma.h", "vc_common.h"):
+    for f in TRAFFIC_SOURCES[kind]:
         with open(os.path.join(ROOT, "compressed_kv_draft_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def stored_traffic(workload: str):
-    """HBM bytes per vc_draft_attn call from the committed counter summary of this
-    workload (profiles/hbm_traffic_draft_<workload>.txt), or None when there is
-    none or the kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_draft_{workload}.txt")
+def stored_traffic(workload: str, kind: str = "draft"):
+    """HBM bytes per vc_draft_attn (kind "draft") or vc_verify_attn ("verify") call
+    from the committed counter summary profiles/hbm_traffic_<kind>_<workload>.txt,
+    or None when there is none or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{kind}_{workload}.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -313,7 +317,7 @@ def stored_traffic(workload: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-    if fields.get("source_sha256") != kernel_source_digest():
+    if fields.get("source_sha256") != kernel_source_digest(kind):
         return None
     try:
         return int(fields["traffic_bytes_per_call"])
@@ -710,7 +714,7 @@ def cycle(a):
     roof = {"bound": "hbm", "kernel": "vc_draft_attn (draft_mfma_kernel<128,4,2> + draft_combine_kernel), int4, "
                                       "one group of 8 sequences",
             "achieved": round(d_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(d_gbs / HBM_PEAK_GBS, 4),
-            "traffic": stored_traffic(w.name + "_cycle"), "bytes_per_launch": int(d_bytes),
+            "traffic": stored_traffic(w.name + "_cycle", "draft"), "bytes_per_launch": int(d_bytes),
             "avg_launch_us": round(1e6 * d_call, 2),
             "how": "draft phase of each half-cycle timed with HIP events on the launch stream, over k calls"}
     line = {
@@ -747,6 +751,7 @@ def cycle(a):
         "verify": {"avg_us": round(1e6 * t_vwhole, 2), "GBps": round(v_gbs, 1), "frac_hbm": round(v_gbs / HBM_PEAK_GBS, 4),
                    "bytes": int(v_bytes), "TFLOPs": round(WL.verify_flops(wg) / t_vwhole / 1e12, 1),
                    "chunked_17_ranges_plus_merge_us": round(1e6 * t_vchunk, 2),
+                   "traffic": stored_traffic(w.name + "_cycle", "verify"),
                    "how": "one group, all pages resident, HIP events"},
         "roofline": roof,
         "full_kv_decode_host_resident": {
@@ -932,7 +937,7 @@ def round_line(w, a, steps, warmup, cpu_units, full_kv):
             if dominant == "draft" else "vc_verify_attn (verify_mfma_kernel + verify_combine_kernel)",
             "achieved": round(d_gbs if dominant == "draft" else v_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round((d_gbs if dominant == "draft" else v_gbs) / HBM_PEAK_GBS, 4),
-            "traffic": stored_traffic(w.name) if dominant == "draft" else None,
+            "traffic": stored_traffic(w.name, dominant),
             "bytes_per_launch": int(d_bytes if dominant == "draft" else v_bytes),
             "avg_launch_us": round(1e6 * (d_avg if dominant == "draft" else v_avg), 2)}
     step_s = wall / steps
@@ -950,10 +955,11 @@ def round_line(w, a, steps, warmup, cpu_units, full_kv):
                    "tokens_per_s_at_n_eq_k": round(w.B * w.n_q / step_s, 1),
                    "tokens_per_s_at_n_eq_25": round(w.B * 26 / step_s, 1)},
         "draft": {"avg_us": round(1e6 * d_avg, 2), "GBps": round(d_gbs, 1), "frac_hbm": round(d_gbs / HBM_PEAK_GBS, 4),
-                  "bytes": int(d_bytes), "ms_per_step": round(draft_total, 4)},
+                  "bytes": int(d_bytes), "ms_per_step": round(draft_total, 4),
+                  "traffic": stored_traffic(w.name, "draft")},
         "verify": {"avg_us": round(1e6 * v_avg, 2), "GBps": round(v_gbs, 1), "frac_hbm": round(v_gbs / HBM_PEAK_GBS, 4),
                    "bytes": int(v_bytes), "TFLOPs": round(WL.verify_flops(w) / v_avg / 1e12, 1),
-                   "ms_per_step": round(verify_total, 4)},
+                   "ms_per_step": round(verify_total, 4), "traffic": stored_traffic(w.name, "verify")},
         "roofline": roof,
         "launch": "each phase (k draft calls | verify | accept) replayed as one recorded HIP graph" if a.graph
                   else "host launches",
