@@ -100,7 +100,9 @@ extern "C" {
  *   All four arrays must be 16-byte aligned for vc_draft_attn.
  *   Dequantised value = fp32(code * scale + zero), a single rounding.
  *   Inputs must keep |q| * K scale < 4096 and |V| scale * 256 < 65504 (the
- *   draft kernel carries these products in f16).
+ *   draft kernel carries these products in f16).  Nothing checks them at run
+ *   time (the values are device data); beyond them the f16 products overflow
+ *   and the results are undefined (in practice inf or NaN).
  * IDENTITY / TOKEN_DROP read k_full / v_full  bf16 [B][Hkv][L_cap][D]; rows
  *   [0, L_full) are context.  keep_idx int32 [B][Hkv][n_keep], sorted,
  *   each in [0, L_full); out-of-range entries are skipped, not dereferenced.
@@ -303,7 +305,8 @@ int vc_draft_attn_noalloc(const vc_kv_comp* comp, const vc_tail* tail, const voi
  * Precision: q.k products on bf16 matrix cores with fp32 accumulation; the
  * softmax in fp32; probabilities rounded to f16 (nearest even) and values
  * converted bf16 -> f16 for the P.V product (fp32 accumulation).  Values must
- * lie in the f16 range (|v| < 65504).
+ * lie in the f16 range (|v| < 65504); larger ones become f16 infinities (not
+ * checked at run time).
  * D in {64, 128}; Hq % Hkv == 0.
  */
 size_t vc_verify_ws_bytes(int B, int Hq, int Hkv, int D, int n_q, int max_ctx);

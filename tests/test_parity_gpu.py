@@ -851,3 +851,82 @@ def test_select_then_token_drop_draft():
                                          tail_v=O.bf16_to_f64(tv[b, h]))
             ref = O.draft_attention_unit(O.bf16_to_f64(q[b, h * g:(h + 1) * g]), keys, vals, scale)
             assert_close(got[b, h * g:(h + 1) * g], ref, f"select+drop b{b} h{h}")
+
+
+def _grid_values(rng, n, s, z, bits):
+    """n x 32 values z + c s on a quantisation grid (each group of 32 holds codes 0
+    and 2^bits - 1, so the group's scale and zero are exactly s and z)."""
+    qmax = (1 << bits) - 1
+    c = rng.integers(0, qmax + 1, (n, 32))
+    c[:, 0], c[:, 1] = 0, qmax
+    return (z + c * s).astype(np.float32)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_draft_at_the_documented_range_limits(bits):
+    """The draft carries q * s_K and p * s_V as f16 products; the header bounds them
+    by |q| s_K < 4096 and s_V * 256 < 65504.  Inputs just inside both bounds:
+    channel 5 of K is an exact grid of scale 240 and head 1's query holds 16 there
+    (|q| s_K = 3840); channel group 0 of V is an exact grid of scale 240 and zero
+    -1792 (s_V * 256 = 61440).  Every grid value is exact in bf16 and the scales
+    and zeros in f16, so the quantiser reproduces them.  The result still
+    matches the oracle."""
+    import torch
+    vc = _vc()
+    from compressed_kv_draft_amd.workload import bf16_dev
+    from synth.gen import f32_to_bf16_bits
+    print(f"[case] draft at the range limits, int{bits}", flush=True)
+    rng = np.random.default_rng(500 + bits)
+    B, Hq, Hkv, D, n, T = 1, 4, 1, 128, 256, 8
+    k = rng.standard_normal((B, Hkv, n + T, D)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, n + T, D)).astype(np.float32)
+    k[0, 0, :n, 5] = _grid_values(rng, n // 32, 240.0, 0.0, bits).reshape(-1)   # K groups: 32 tokens of a channel
+    v[0, 0, :n, :32] = _grid_values(rng, n, 240.0, -1792.0, bits)               # V groups: 32 channels of a token
+    q = rng.standard_normal((B, Hq, D)).astype(np.float32) * 2.0
+    q[0, 1, 5] = 16.0
+    kb, vb, qb = (f32_to_bf16_bits(x) for x in (k, v, q))
+    comp = vc.quantize_kv(bf16_dev(kb, "cuda"), bf16_dev(vb, "cuda"), bits, n)
+    # the grid survived quantisation: the scales are exactly 250
+    km = vc.unpack_quant(comp, B, Hkv, D)[2].cpu().numpy()
+    vm = vc.unpack_quant(comp, B, Hkv, D)[3].cpu().numpy()
+    assert (km[0, 0, :, 5, 0] == 240.0).all() and (vm[0, 0, :, 0, 0] == 240.0).all()
+    tail = vc.Tail(bf16_dev(np.ascontiguousarray(kb[:, :, n:]), "cuda"), bf16_dev(np.ascontiguousarray(vb[:, :, n:]), "cuda"),
+                   torch.full((B,), T, dtype=torch.int32, device="cuda"))
+    scale = O.scale_for(D)
+    got = vc.draft_attn(comp, tail, bf16_dev(qb, "cuda"), scale).cpu().numpy()
+    kf = O.bf16_to_f64(kb[0, 0, :n]).astype(np.float32)
+    vf = O.bf16_to_f64(vb[0, 0, :n]).astype(np.float32)
+    keys, vals = O.draft_kv_rows("quant", k_deq=O.dequant_k(*O.quantize_k(kf, bits)),
+                                 v_deq=O.dequant_v(*O.quantize_v(vf, bits)),
+                                 tail_k=O.bf16_to_f64(kb[0, 0, n:]), tail_v=O.bf16_to_f64(vb[0, 0, n:]))
+    want = O.draft_attention_unit(O.bf16_to_f64(qb[0]), keys, vals, scale)
+    assert_close(got[0], want, f"range limits int{bits}")
+
+
+def test_verify_at_the_value_range_limit():
+    """Verify converts V from bf16 to f16 for the P.V product; the header bounds
+    |v| < 65504.  Rows of +-59904 (the bf16 value nearest 60000 below it) among
+    N(0,1) rows still match the oracle."""
+    import torch
+    vc = _vc()
+    from compressed_kv_draft_amd.workload import bf16_dev
+    from synth.gen import f32_to_bf16_bits
+    print("[case] verify at the value range limit", flush=True)
+    rng = np.random.default_rng(510)
+    B, Hq, Hkv, D, L, n_q = 2, 8, 2, 128, 300, 5
+    k = rng.standard_normal((B, Hkv, L + n_q, D)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, L + n_q, D)).astype(np.float32)
+    v[:, :, ::7, ::3] = 59904.0 * np.sign(rng.standard_normal((B, Hkv, (L + n_q + 6) // 7, (D + 2) // 3)))
+    q = rng.standard_normal((B, Hq, n_q, D)).astype(np.float32)
+    kb, vb, qb = (f32_to_bf16_bits(x) for x in (k, v, q))
+    assert (O.bf16_to_f64(vb).max() == 59904.0)
+    full = vc.FullKV(bf16_dev(kb, "cuda"), bf16_dev(vb, "cuda"), L_cap=L + n_q)
+    ctx = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    scale = O.scale_for(D)
+    got = vc.verify_attn(bf16_dev(qb, "cuda"), full, ctx, L, Hkv, scale).cpu().numpy()
+    g = Hq // Hkv
+    for b in range(B):
+        for h in range(Hkv):
+            want = O.verify_attention_unit(O.bf16_to_f64(qb[b, h * g:(h + 1) * g]), O.bf16_to_f64(kb[b, h]),
+                                           O.bf16_to_f64(vb[b, h]), L, scale)
+            assert_close(got[b, h * g:(h + 1) * g], want, f"verify |v| limit b{b} h{h}")
