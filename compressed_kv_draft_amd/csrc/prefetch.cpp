@@ -34,12 +34,18 @@ bool is_pinned(const void* p) {
   return attr.type == hipMemoryTypeHost;
 }
 
+constexpr size_t kGatherThreads = 4;
+
 // Copy `n` pages (src slot list -> consecutive staging pages) with up to
-// `threads` host threads.
+// kGatherThreads host threads.
 void gather_pages(const char* pool, const std::vector<int32_t>& slots, size_t page_bytes, char* staging) {
   const size_t n = slots.size();
+  // Four threads keep up with the host-to-device DMA; more of them compete
+  // with it for host memory bandwidth.  Measured on MI355X with the Llama-70B-
+  // shaped cycle (two 2 GiB group transfers per cycle): 2 threads 105 ms per
+  // cycle, 3: 80, 4: 78, 6: 82, 8: 85, 12 and 16: 90.
   unsigned hw = std::thread::hardware_concurrency();
-  size_t threads = std::min<size_t>(hw == 0 ? 4 : hw, 8);  // leave cores for the caller's own threads
+  size_t threads = std::min<size_t>(hw == 0 ? 4 : hw, kGatherThreads);
   threads = std::min(threads, (n + 63) / 64);  // at least 64 pages per thread
   if (threads <= 1) {
     for (size_t k = 0; k < n; ++k) std::memcpy(staging + k * page_bytes, pool + (size_t)slots[k] * page_bytes, page_bytes);
