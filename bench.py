@@ -36,6 +36,8 @@ def parse():
     p.add_argument("--leg-steps", type=int, default=10)
     p.add_argument("--leg-warmup", type=int, default=15)
     p.add_argument("--leg-cpu-units", type=int, default=2)
+    p.add_argument("--no-e2e-leg", action="store_true",
+                   help="leave out the tiny decoder's end-to-end rate from the default line")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", action="store_true",
                    help="replay each phase of the round (k draft calls, verify, accept) as a recorded HIP graph "
@@ -370,13 +372,13 @@ def cpu_baseline(w, dw, n_accept_sum, units):
                       f"fp64 numpy, {dt:.1f} s measured, scaled x{(w.B * w.Hkv) / len(picks):.0f}"}
 
 
-def e2e(a):
+def e2e_record(steps: int, warmup: int, with_eager: bool = True):
     """Tiny decoder end to end: prefill, then 256 greedy tokens by the loop.
     Every attention and token decision runs in libvc; the dense layers are
     torch fp32.  Drafting replays one recorded HIP graph per position (the
-    eager rate is reported beside it).  Reports decode tokens/s (prefill
-    excluded), the accepted-count histogram, and whether the tokens equal the
-    stored oracle sequence."""
+    eager rate is reported beside it when with_eager).  Returns decode
+    tokens/s (prefill excluded), the accepted-count histogram, and whether the
+    tokens equal the stored oracle sequence."""
     import numpy as np
     import torch
 
@@ -387,17 +389,18 @@ def e2e(a):
     W = M.weights(cfg)
     cos, sin = M.rope_tables(cfg)
     prompt = M.prompt(cfg)
+
     def timed(graph):
         runs = []
-        for i in range(a.warmup_e2e + a.steps_e2e):
+        for i in range(warmup + steps):
             lm = TinyLM(cfg, W, cos, sin)
             toks, acc, st = lm.generate(prompt, cfg.n_gen, graph=graph)
-            if i >= a.warmup_e2e:
+            if i >= warmup:
                 runs.append((toks, acc, st))
             del lm
             torch.cuda.empty_cache()
         return runs
-    eager = timed(False)
+    eager = timed(False) if with_eager else []
     runs = timed(True)
     gold = None
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tests", "golden", f"e2e_{cfg.name}.txt")
@@ -408,21 +411,26 @@ def e2e(a):
     dec = [r[2]["decode_s"] for r in runs]
     toks, acc, st = runs[int(np.argmin(dec))]
     hist = {str(k): int(v) for k, v in zip(*np.unique(acc, return_counts=True))}
-    line = {"metric": "end-to-end verified tokens/s (tiny decoder, draft-then-verify, greedy)",
-            "value": round((cfg.n_gen - 1) / min(dec), 1), "unit": "tokens/s", "n_gpus": 1,
-            "steps": a.steps_e2e, "warmup": a.warmup_e2e, "higher_is_better": True, "data": "synthetic",
-            "config": {"workload": cfg.name, "layers": cfg.n_layers, "d_model": cfg.d_model, "q_heads": cfg.Hq,
-                       "kv_heads": cfg.Hkv, "head_dim": cfg.D, "ffn": cfg.ffn, "vocab": cfg.vocab,
-                       "prompt": cfg.prompt, "draft_len": cfg.k, "generated": cfg.n_gen, "draft_cache": "int4",
-                       "dense_layers": "torch fp32 (outside the measured path)"},
-            "rounds": st["rounds"], "accepted_per_round": acc, "accepted_histogram": hist,
-            "mean_tokens_per_round": round(float(np.mean(np.array(acc) + 1)), 2),
-            "decode_s": [round(x, 4) for x in dec], "prefill_s": round(st["prefill_s"], 4),
-            "drafting": "one HIP graph per draft position, replayed k times per round",
-            "eager_value": round((cfg.n_gen - 1) / min(r[2]["decode_s"] for r in eager), 1),
-            "graph_equals_eager": all(r[0] == toks and r[1] == acc for r in eager),
-            "equals_oracle_greedy": (toks == gold) if gold is not None else None}
-    print(json.dumps(line), flush=True)
+    rec = {"metric": "end-to-end verified tokens/s (tiny decoder, draft-then-verify, greedy)",
+           "value": round((cfg.n_gen - 1) / min(dec), 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": steps, "warmup": warmup, "higher_is_better": True, "data": "synthetic",
+           "config": {"workload": cfg.name, "layers": cfg.n_layers, "d_model": cfg.d_model, "q_heads": cfg.Hq,
+                      "kv_heads": cfg.Hkv, "head_dim": cfg.D, "ffn": cfg.ffn, "vocab": cfg.vocab,
+                      "prompt": cfg.prompt, "draft_len": cfg.k, "generated": cfg.n_gen, "draft_cache": "int4",
+                      "dense_layers": "torch fp32 (outside the measured path)"},
+           "rounds": st["rounds"], "accepted_per_round": acc, "accepted_histogram": hist,
+           "mean_tokens_per_round": round(float(np.mean(np.array(acc) + 1)), 2),
+           "decode_s": [round(x, 4) for x in dec], "prefill_s": round(st["prefill_s"], 4),
+           "drafting": "one HIP graph per draft position, replayed k times per round",
+           "equals_oracle_greedy": (toks == gold) if gold is not None else None}
+    if with_eager:
+        rec["eager_value"] = round((cfg.n_gen - 1) / min(r[2]["decode_s"] for r in eager), 1)
+        rec["graph_equals_eager"] = all(r[0] == toks and r[1] == acc for r in eager)
+    return rec
+
+
+def e2e(a):
+    print(json.dumps(e2e_record(a.steps_e2e, a.warmup_e2e)), flush=True)
 
 
 def e2e_groups(a):
@@ -782,6 +790,14 @@ def cycle(a):
         print(f"[leg] {name}: draft {r['draft']['avg_us']} us ({r['draft']['frac_hbm']}), verify "
               f"{r['verify']['avg_us']} us ({r['verify']['frac_hbm']}), {time.perf_counter() - t:.1f} s", flush=True)
     line["other_workloads"] = legs
+    if not a.no_e2e_leg:
+        t = time.perf_counter()
+        r = e2e_record(1, 1, with_eager=False)
+        line["end_to_end"] = {k: r[k] for k in ("value", "unit", "config", "rounds", "accepted_histogram",
+                                                "mean_tokens_per_round", "decode_s", "prefill_s", "drafting",
+                                                "equals_oracle_greedy")}
+        print(f"[e2e] {r['value']} tokens/s, equals oracle greedy: {r['equals_oracle_greedy']}, "
+              f"{time.perf_counter() - t:.1f} s", flush=True)
     print(json.dumps(line), flush=True)
 
 
