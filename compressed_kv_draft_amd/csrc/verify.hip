@@ -308,7 +308,7 @@ __global__ __launch_bounds__(64 * NW) void verify_mfma_kernel(VerifyArgs a) {
         for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int e = 0; e < 4; ++e) xv[4 * h + e] = fmaf(s[i][h][e], a.scale_log2, -mu[i]);
-        if (need_mask) {
+        if (__builtin_expect(need_mask, 0)) {
           // key t0 + 16h + 4q + e is visible iff lo <= 16h + e <= lim
           const int lim = min(rlim[i], ke - 1) - t0 - 4 * quad;
           const int lo = a.key_lo - t0 - 4 * quad;
