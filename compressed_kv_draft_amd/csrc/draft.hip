@@ -254,23 +254,26 @@ struct RowSrc {
   int bound;           // physical rows in [0, bound) are readable
 };
 
+// The kept-row index (or the row itself) of logical row blk * 32 + (lane & 31),
+// unchecked; -1 past the valid rows.  Loaded a block ahead of its use, so that
+// a block's row loads wait for one memory latency, not for two in sequence.
+__device__ __forceinline__ int block_row_index(const RowSrc& src, int blk, int lane) {
+  const int t = blk * 32 + (lane & 31);
+  if (t >= src.n_valid) return -1;
+  return src.idx != nullptr ? src.idx[t] : t;
+}
+
 // One block of 32 exact rows: q.k on bf16 matrix cores, P.V with P = hi + lo in
-// bf16 and V staged in LDS, read transposed.
+// bf16 and V staged in LDS, read transposed.  p: block_row_index of this block.
 template <int D, int NV>
-__device__ __forceinline__ void rows_block(const RowSrc& src, int blk, const bf16x8 (&qb)[D / 32], float scale_log2,
-                                           uint16_t* vst, State<D / 16, NV>& st, int lane, int col, int quad,
-                                           int hilo) {
+__device__ __forceinline__ void rows_block(const RowSrc& src, int blk, int p, const bf16x8 (&qb)[D / 32],
+                                           float scale_log2, uint16_t* vst, State<D / 16, NV>& st, int lane,
+                                           int col, int quad, int hilo) {
   constexpr int NKS = D / 32, NCT = D / 16, VPITCH = D + 16;
   const int t0 = blk * 32;
-  // physical row of logical row t0 + (lane & 31), or -1
-  int myrow = -1;
-  {
-    const int t = t0 + (lane & 31);
-    if (t < src.n_valid) {
-      const int p = src.idx != nullptr ? src.idx[t] : t;
-      myrow = (p >= 0 && p < src.bound) ? p : -1;
-    }
-  }
+  // physical row of logical row t0 + (lane & 31), or -1 (past the valid rows,
+  // or an index outside [0, bound): skipped, never dereferenced)
+  const int myrow = (p >= 0 && p < src.bound) ? p : -1;
   // K rows of tokens col and 16 + col; k-step ks takes channels 32 ks + 8 quad
   // .. + 7, so the four quads of a row read 64 contiguous bytes per load
   u32x4 kr[2][NKS];
@@ -331,6 +334,20 @@ __device__ __forceinline__ void rows_block(const RowSrc& src, int blk, const bf1
     const s16x4 hi4 = lds_read_tr16(base + (16 + 4 * quad + (col >> 2)) * VPITCH);
     const s16x8 bv8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
     st.O[ct] = mfma_bf16(A, __builtin_bit_cast(bf16x8, bv8), st.O[ct]);
+  }
+}
+
+// This wavefront's exact-row blocks first, first + kWaves, ... below end, each
+// block's row indices loaded while the previous block is computed.
+template <int D, int NV>
+__device__ __forceinline__ void rows_loop(const RowSrc& src, int first, int end, const bf16x8 (&qb)[D / 32],
+                                          float scale_log2, uint16_t* vst, State<D / 16, NV>& st, int lane,
+                                          int col, int quad, int hilo) {
+  int p_next = first < end ? block_row_index(src, first, lane) : -1;
+  for (int blk = first; blk < end; blk += kWaves) {
+    const int p = p_next;
+    if (blk + kWaves < end) p_next = block_row_index(src, blk + kWaves, lane);
+    rows_block<D, NV>(src, blk, p, qb, scale_log2, vst, st, lane, col, quad, hilo);
   }
 }
 
@@ -481,8 +498,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
     const int bhi = min(blo + a.tail_bpw, nb);
     bf16x8 qb[NKS];
     load_qb(qb);
-    for (int blk = blo + wave; blk < bhi; blk += kWaves)
-      rows_block<D, NV>(src, blk, qb, a.scale_log2, vst, st, lane, col, quad, hilo);
+    rows_loop<D, NV>(src, blo + wave, bhi, qb, a.scale_log2, vst, st, lane, col, quad, hilo);
     finish(a.main_splits + split - a.tail_first, false);
     st.clear();
     __syncthreads();  // the epilogue's LDS is reused below
@@ -691,8 +707,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
       src.bound = a.row_bound;
       bf16x8 qb[NKS];
       load_qb(qb);
-      for (int blk = blo + wave; blk < bhi; blk += kWaves)
-        rows_block<D, NV>(src, blk, qb, a.scale_log2, vst, st, lane, col, quad, hilo);
+      rows_loop<D, NV>(src, blo + wave, bhi, qb, a.scale_log2, vst, st, lane, col, quad, hilo);
     }
   }
   finish(split, true);
