@@ -300,12 +300,15 @@ TRAFFIC_SOURCES = {"draft": ("draft.hip", "lds_dma.h", "mfma.h", "vc_common.h"),
 
 
 def kernel_source_digest(kind="draft"):
-    """sha256 of a kernel's sources: ties a stored counter reading to the code it was taken on."""
+    """sha256 of a kernel's sources and of the compiler flags of its file: ties a
+    stored counter reading to the code it was taken on."""
     import hashlib
+    from compressed_kv_draft_amd import build as B
     h = hashlib.sha256()
     for f in TRAFFIC_SOURCES[kind]:
         with open(os.path.join(ROOT, "compressed_kv_draft_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
+    h.update(" ".join(B.FLAGS + B.FILE_FLAGS.get(TRAFFIC_SOURCES[kind][0], [])).encode())
     return h.hexdigest()
 
 
