@@ -266,13 +266,12 @@ __device__ __forceinline__ int block_row_index(const RowSrc& src, int blk, int l
 // One block of 32 exact rows: q.k on bf16 matrix cores, P.V with P = hi + lo in
 // bf16 and V staged in LDS, read transposed.  p: block_row_index of this block.
 template <int D, int NV>
-__device__ __forceinline__ void rows_block(const RowSrc& src, int blk, int p, const bf16x8 (&qb)[D / 32],
-                                           float scale_log2, uint16_t* vst, State<D / 16, NV>& st, int lane,
-                                           int col, int quad, int hilo) {
+__device__ __forceinline__ void rows_block(const RowSrc& src, int p, const bf16x8 (&qb)[D / 32], float scale_log2,
+                                           uint16_t* vst, State<D / 16, NV>& st, int lane, int col, int quad,
+                                           int hilo) {
   constexpr int NKS = D / 32, NCT = D / 16, VPITCH = D + 16;
-  const int t0 = blk * 32;
-  // physical row of logical row t0 + (lane & 31), or -1 (past the valid rows,
-  // or an index outside [0, bound): skipped, never dereferenced)
+  // physical row of this lane's logical row (lane & 31) of the block, or -1 (past
+  // the valid rows, or an index outside [0, bound): skipped, never dereferenced)
   const int myrow = (p >= 0 && p < src.bound) ? p : -1;
   // K rows of tokens col and 16 + col; k-step ks takes channels 32 ks + 8 quad
   // .. + 7, so the four quads of a row read 64 contiguous bytes per load
@@ -347,7 +346,7 @@ __device__ __forceinline__ void rows_loop(const RowSrc& src, int first, int end,
   for (int blk = first; blk < end; blk += kWaves) {
     const int p = p_next;
     if (blk + kWaves < end) p_next = block_row_index(src, blk + kWaves, lane);
-    rows_block<D, NV>(src, blk, p, qb, scale_log2, vst, st, lane, col, quad, hilo);
+    rows_block<D, NV>(src, p, qb, scale_log2, vst, st, lane, col, quad, hilo);
   }
 }
 
