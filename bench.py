@@ -789,6 +789,11 @@ def cycle(a):
                   "draft_ms_per_half": round(1e3 * d_call * w.k, 3),
                   "verify_tail_after_last_chunk_ms": round(1e3 * tail, 3),
                   "compute_per_half_ms": round(1e3 * (d_alone * w.k + t_vchunk), 3),
+                  "compute_hidden_under_transfer": round(min(1.0, max(0.0, (
+                      G * (d_alone * w.k + t_vchunk) + pcie_only - cycle_s) / (G * (d_alone * w.k + t_vchunk)))), 4),
+                  "compute_hidden_how": "share of the cycle's GPU work (each half's k draft calls alone plus its "
+                                        "chunked verify alone) that adds no time over the copy-only transfers: "
+                                        "(compute + copy-only - cycle) / compute, clipped to [0, 1]",
                   "draft_in_cycle_over_continuous": round(d_call / d_alone, 4),
                   "chunked_vs_whole_verify_rel_l2": max(rel)},
         "draft": {"avg_us": round(1e6 * d_call, 2), "GBps": round(d_gbs, 1), "frac_hbm": round(d_gbs / HBM_PEAK_GBS, 4),
