@@ -49,7 +49,8 @@ def parse():
     p.add_argument("--no-full-kv-decode", action="store_true",
                    help="skip the full-KV decode baseline (keeps per-kernel profiles to the path's own calls)")
     p.add_argument("--cpu-units", type=int, default=None,
-                   help="(b, kv-head) units in the CPU oracle sample (default 8 for a round, 2 for the cycle)")
+                   help="(b, kv-head) units in the CPU oracle sample (default 8 for a round, 24 for the cycle: "
+                        "about 10-15 s of oracle work)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain 1 GiB device-to-device copy, 3 times (the reference kernel for "
                         "scaling the FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -818,7 +819,7 @@ def cycle(a):
     print(f"[cycle] {value:.1f} verified tok/s, cycle {1e3 * cycle_s:.2f} ms (PCIe only {1e3 * pcie_only:.2f}), "
           f"draft {1e6 * d_call:.1f} us/call ({d_gbs / HBM_PEAK_GBS:.3f} of HBM), verify {1e6 * t_vwhole:.1f} us",
           flush=True)
-    units = 0 if a.no_cpu_baseline else (2 if a.cpu_units is None else a.cpu_units)
+    units = 0 if a.no_cpu_baseline else (24 if a.cpu_units is None else a.cpu_units)
     if units:
         line["cpu_baseline"] = cycle_cpu_baseline(w, cw, tokens, units)
     del cw, staging, parts
@@ -853,9 +854,10 @@ def cycle_cpu_baseline(w, cw, tokens_per_cycle, units):
     (no transfer is modelled on the CPU side)."""
     import numpy as np
     from oracle import round as R
+    import compressed_kv_draft_amd.workload as WL
     wg = w.with_(B=cw.bg)
     g = w.g
-    picks = [(u // w.Hkv, u % w.Hkv) for u in range(min(units, 2 * w.Hkv))]
+    picks = [(u // w.Hkv, u % w.Hkv) for u in range(min(units, WL.CPU_SAMPLE_SEQS * w.Hkv))]
     comps = {}
     for (b, h) in picks:
         comps[(b, h)] = R.unit_compressed(wg, cw.np_ctx["K"][b, h], cw.np_ctx["V"][b, h])
@@ -880,7 +882,6 @@ def cycle_cpu_baseline(w, cw, tokens_per_cycle, units):
                     break
     except OSError:
         pass
-    import compressed_kv_draft_amd.workload as WL
     cyc_bytes = w.groups * (sum(WL.draft_step_bytes(wg, j) for j in range(w.k)) + WL.verify_bytes(wg))
     return {"value": tokens_per_cycle / full, "unit": "verified tokens/s", "cores": cores, "kind": "oracle",
             "cpu_model": model, "effective_GBps": round(cyc_bytes / full / 1e9, 3),

@@ -15,6 +15,10 @@ from synth.configs import Workload
 from . import _lib as vc
 
 
+# sequences of the cycle workload kept on the host for the CPU oracle sample
+CPU_SAMPLE_SEQS = 3
+
+
 def bf16_dev(bits: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
 
@@ -265,7 +269,8 @@ class CycleWorkload:
             self.q_steps.append([qv[:, :, j, :].contiguous() for j in range(w.k)])
             self.full.append(vc.FullKV(self.pool, None, 0, torch.from_numpy(tab).to(device), pt, pps, n_dev_pages))
             if gi == 0:
-                self.np_ctx = {"K": K[:2].copy(), "V": V[:2].copy()}   # two sequences for the CPU baseline sample
+                # the first sequences of group 0, for the CPU baseline sample
+                self.np_ctx = {"K": K[:CPU_SAMPLE_SEQS].copy(), "V": V[:CPU_SAMPLE_SEQS].copy()}
             del K, V
         self.np_q, self.np_kn, self.np_vn = Q, Kn, Vn
         self.ctx_len = torch.full((bg,), w.L, dtype=torch.int32, device=device)
