@@ -15,7 +15,7 @@ from synth.configs import Workload
 from . import _lib as vc
 
 
-# sequences of the cycle workload kept on the host for the CPU oracle sample
+# sequences of the cycle workload kept on the host for the CPU baseline sample
 CPU_SAMPLE_SEQS = 3
 
 
