@@ -38,9 +38,9 @@ namespace vc {
 namespace {
 
 struct DraftArgs {
-  int n_main;    // rows of the compressed part (quant: n_quant; identity: L_full; drop: n_keep)
-  int q_cap;  // quant: rows per unit the code/meta arrays hold (their stride)
-  int L_cap;
+  int n_main;     // rows of the compressed part (quant: n_quant; identity: L_full; drop: n_keep)
+  int q_cap;      // quant: rows per unit the code/meta arrays hold (their stride)
+  int L_cap;      // identity / drop: rows per unit of k_full / v_full (their stride)
   int row_bound;  // valid physical rows of k_full/v_full (identity / drop)
   const uint8_t* k_codes;
   const uint8_t* v_codes;
@@ -179,9 +179,6 @@ __device__ __forceinline__ float swap_adjacent(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
 }
 
-__device__ __forceinline__ float f16lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[0]; }
-__device__ __forceinline__ float f16hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[1]; }
-
 // Per-lane softmax state: running max m (log2 units) of this lane's head, the
 // offset mu the scores are taken relative to (m, or 0 while m is -inf), the
 // amount thr a block max must exceed to move m (-inf while m is -inf, else
@@ -205,8 +202,9 @@ struct State {
 };
 
 // Online softmax over the 8 scores a lane holds for one block (its head, tokens
-// 4q..4q+3 and 16+4q..16+4q+3).  Scores arrive relative to st.mu.  The running max only moves when some score exceeds it by kTau, so
-// in the common case no cross-lane reduction and no rescale happen; P <= 2^kTau.
+// 4q..4q+3 and 16+4q..16+4q+3).  Scores arrive relative to st.mu.  The running
+// max only moves when some score exceeds it by kTau, so in the common case no
+// cross-lane reduction and no rescale happen; P <= 2^kTau.
 template <int NCT, int NV>
 __device__ __forceinline__ void softmax_block(float (&x)[8], State<NCT, NV>& st, float (&P)[8], int quad) {
   float tl = x[0];
@@ -264,15 +262,16 @@ __device__ __forceinline__ int block_row_index(const RowSrc& src, int blk, int l
 }
 
 // One block of 32 exact rows: q.k on bf16 matrix cores, P.V with P = hi + lo in
-// bf16 and V staged in LDS, read transposed.  p: block_row_index of this block.
+// bf16 and V staged in LDS, read transposed.  row_idx: block_row_index of this
+// block for this lane.
 template <int D, int NV>
-__device__ __forceinline__ void rows_block(const RowSrc& src, int p, const bf16x8 (&qb)[D / 32], float scale_log2,
-                                           uint16_t* vst, State<D / 16, NV>& st, int lane, int col, int quad,
-                                           int hilo) {
+__device__ __forceinline__ void rows_block(const RowSrc& src, int row_idx, const bf16x8 (&qb)[D / 32],
+                                           float scale_log2, uint16_t* vst, State<D / 16, NV>& st, int lane,
+                                           int col, int quad, int hilo) {
   constexpr int NKS = D / 32, NCT = D / 16, VPITCH = D + 16;
   // physical row of this lane's logical row (lane & 31) of the block, or -1 (past
   // the valid rows, or an index outside [0, bound): skipped, never dereferenced)
-  const int myrow = (p >= 0 && p < src.bound) ? p : -1;
+  const int myrow = (row_idx >= 0 && row_idx < src.bound) ? row_idx : -1;
   // K rows of tokens col and 16 + col; k-step ks takes channels 32 ks + 8 quad
   // .. + 7, so the four quads of a row read 64 contiguous bytes per load
   u32x4 kr[2][NKS];
@@ -342,11 +341,11 @@ template <int D, int NV>
 __device__ __forceinline__ void rows_loop(const RowSrc& src, int first, int end, const bf16x8 (&qb)[D / 32],
                                           float scale_log2, uint16_t* vst, State<D / 16, NV>& st, int lane,
                                           int col, int quad, int hilo) {
-  int p_next = first < end ? block_row_index(src, first, lane) : -1;
+  int idx_next = first < end ? block_row_index(src, first, lane) : -1;
   for (int blk = first; blk < end; blk += kWaves) {
-    const int p = p_next;
-    if (blk + kWaves < end) p_next = block_row_index(src, blk + kWaves, lane);
-    rows_block<D, NV>(src, p, qb, scale_log2, vst, st, lane, col, quad, hilo);
+    const int idx = idx_next;
+    if (blk + kWaves < end) idx_next = block_row_index(src, blk + kWaves, lane);
+    rows_block<D, NV>(src, idx, qb, scale_log2, vst, st, lane, col, quad, hilo);
   }
 }
 
@@ -483,7 +482,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
   // (the last workgroups first take a range of the exact rows, as a partial
   // of their own, then a correspondingly smaller range of the compressed part)
   if (split >= a.tail_first && a.T_cap > 0) {
-    int tl = a.T_cap > 0 ? a.tail_len[b] : 0;
+    int tl = a.tail_len[b];
     tl = tl < 0 ? 0 : (tl > a.T_cap ? a.T_cap : tl);
     RowSrc src;
     src.k = a.tail_k;
@@ -521,7 +520,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D,
         qraw[ks] = *reinterpret_cast<const u32x4*>(qhead + quad * (D / 4) + 8 * ks);
       uint32_t qF[NKS][4];
       uint32_t* zero = reinterpret_cast<uint32_t*>(smem + C::ZERO_OFF);
-      uint32_t* qzt = reinterpret_cast<uint32_t*>(smem + C::QZ_OFF);  // [ks][quad][head][4]: a quad's heads in consecutive 16-byte chunks
+      // [ks][quad][head][4]: a quad's heads in consecutive 16-byte chunks
+      uint32_t* qzt = reinterpret_cast<uint32_t*>(smem + C::QZ_OFF);
       {
         const uint16_t* qh = reinterpret_cast<const uint16_t*>(qraw);
 #pragma unroll

@@ -6,17 +6,19 @@
 //
 // The g query heads of a GQA group times the n_q positions form R = g * n_q
 // query rows that share one KV head, so q.K^T and P.V are real contractions.
-// Per 32-key tile a workgroup (4 or 8 wavefronts) stages K (bf16, padded rows)
-// and V (converted to f16) in LDS once; every wavefront owns up to MT 16-row
-// query tiles and computes, for each,
+// Per 32-key tile a workgroup (4 or 8 wavefronts) stages K (bf16) and V
+// (converted to f16) in LDS once, rows XOR-swizzled; every wavefront owns up to
+// MT 16-row query tiles and computes, for each,
 //   S[32 keys x 16 rows] = K . Q^T   (bf16 MFMA: keys are the A rows, so each
 //                                     lane ends up with 8 keys of one row)
 //   online softmax per row in fp32 (lazy rescale, running max moves by >= 2^8)
 //   O[16 rows x D]     += P . V      (f16 MFMA; P rounded to nearest even; V
 //                                     read transposed with ds_read_b64_tr_b16)
 // The K and V operands of a tile are read from LDS once per wavefront and
-// shared by its query tiles.  LDS is double-buffered with one barrier per tile;
-// the next tile's global loads are in flight during the current tile's math.
+// shared by its query tiles.  The tiles stream through a ring of kDepth LDS
+// slots by direct global->LDS loads issued kDepth - 1 tiles ahead, with one
+// barrier per tile, so the next tiles' loads are in flight during this tile's
+// math.
 // A workgroup has 8 wavefronts when 4 cannot hold every query tile (a GQA group
 // of 8 at k = 32 has 17), so that the cache is read from HBM once.  Query rows
 // beyond 3 tiles per wavefront go to further row groups, laid out so that the
