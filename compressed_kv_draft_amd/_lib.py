@@ -310,7 +310,7 @@ def draft_attn(comp: Compressed, tail: Tail, q: torch.Tensor, scale: float, out=
         n_main = comp.t.get("n_quant", 0) if comp.kind == "quant" else (
             comp.t.get("n_keep", 0) if comp.kind == "token_drop" else comp.t.get("L_full", 0))
         need = draft_ws_bytes(B, Hq, Hkv, D, n_main + tail.desc.T_cap)
-        ws = torch.zeros(need, dtype=torch.uint8, device=q.device)  # counters start at zero
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)  # every partial read is written by the call
     rc = LIB.vc_draft_attn(ctypes.byref(comp.desc), ctypes.byref(tail.desc), _ptr(q), _ptr(out), _ptr(lse),
                            B, Hq, Hkv, D, float(scale), _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, "vc_draft_attn")

@@ -262,8 +262,9 @@ int vc_debug_dequant(const vc_kv_comp* comp, int B, int Hkv, int D, int b, int h
  *   lse  device fp32 [B][Hq] or NULL: natural log of sum_t exp(scale q.k_t)
  *   ws   device workspace of at least vc_draft_ws_bytes(B, Hq, Hkv, D,
  *        n_main + T_cap) bytes, 16-byte aligned (n_main = n_quant, L_full or
- *        n_keep).  QUANT codes must be 16-byte aligned, V meta 8-byte.  A sequence with no key at all
- *        gets o = 0 and lse = -inf.
+ *        n_keep).  QUANT codes must be 16-byte aligned, V meta 8-byte.
+ * A sequence with no key at all (an empty compressed part and a zero tail
+ * length) gets o = 0 and lse = -inf.
  * D in {64, 128}; Hq % Hkv == 0; Hq / Hkv <= 8.
  */
 size_t vc_draft_ws_bytes(int B, int Hq, int Hkv, int D, int max_keys);

@@ -174,6 +174,19 @@ def draft_attention_unit(q_heads: np.ndarray, keys: np.ndarray, values: np.ndarr
     return softmax_attention(q_heads, keys, values, scale)
 
 
+def draft_lse_unit(q_heads: np.ndarray, keys: np.ndarray, scale: float) -> np.ndarray:
+    """Natural log of the softmax denominator of each query head [g, D] over keys
+    [n, D]: ln sum_t exp(scale q . k_t) (the normaliser of the attention above,
+    written out; -inf when there is no key).  Shifted by the row maximum before
+    the exponentials, which leaves the value unchanged."""
+    g = q_heads.shape[0]
+    if keys.shape[0] == 0:
+        return np.full(g, -np.inf)
+    s = (q_heads @ keys.T) * scale              # [g, n]
+    m = s.max(axis=1)
+    return m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+
+
 def gqa_kv_head(h: int, Hq: int, Hkv: int) -> int:
     """Reading: query head h reads KV head floor(h * Hkv / Hq) (contiguous groups)."""
     return (h * Hkv) // Hq

@@ -261,6 +261,46 @@ def test_dequant_v_and_logits_pins_catch_planted_mistakes():
             pin_logits(bad)
 
 
+def pin_draft_lse(lse):
+    """The log-sum-exp of the draft scores: one key gives its scaled score
+    exactly; n equal keys give ln n plus that score; a random case equals the
+    sum of exponentials written out with math.fsum; no key gives -inf."""
+    q = np.array([[1.0, 2.0], [-0.5, 0.25]])
+    k1 = np.array([[3.0, -1.0]])
+    # scores 0.5 (1*3 - 2*1) = 0.5 and 0.5 (-1.5 - 0.25) = -0.875
+    assert list(lse(q, k1, 0.5)) == [0.5, -0.875]
+    kn = np.repeat(k1, 5, axis=0)
+    assert np.allclose(lse(q, kn, 0.5), [0.5 + math.log(5), -0.875 + math.log(5)], atol=1e-15, rtol=0)
+    rng = np.random.default_rng(31)
+    q = rng.standard_normal((3, 8))
+    keys = rng.standard_normal((11, 8))
+    want = [math.log(math.fsum(math.exp(0.3 * float(q[i] @ keys[t])) for t in range(11))) for i in range(3)]
+    assert np.allclose(lse(q, keys, 0.3), want, atol=1e-13, rtol=0)
+    assert list(lse(q, keys[:0], 0.3)) == [-np.inf] * 3
+
+
+def test_draft_lse_pin():
+    pin_draft_lse(O.draft_lse_unit)
+
+
+def test_draft_lse_pin_catches_planted_mistakes():
+    def lse_log2(q, keys, scale):
+        return O.draft_lse_unit(q, keys, scale) / math.log(2)
+
+    def lse_unscaled(q, keys, scale):
+        return O.draft_lse_unit(q, keys, 1.0)
+
+    def lse_max_only(q, keys, scale):
+        return (q @ keys.T * scale).max(axis=1) if len(keys) else np.full(len(q), -np.inf)
+
+    def lse_mean(q, keys, scale):
+        return O.draft_lse_unit(q, keys, scale) - (math.log(len(keys)) if len(keys) else 0.0)
+
+    for bad in (lse_log2, lse_unscaled, lse_max_only, lse_mean):
+        with pytest.raises(AssertionError):
+            pin_draft_lse(bad)
+
+
 # -------------------------------------------------------------- attention ---
 
 def pin_attention_closed_forms(attn):

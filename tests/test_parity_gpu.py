@@ -539,6 +539,77 @@ def test_draft_ragged_tail_lengths(bits):
             assert_close(got[b, h * g:(h + 1) * g], ref, f"ragged tail int{bits} b{b} h{h}")
 
 
+def _assert_lse(got, ref, what):
+    """lse to the attention bar: finite rows within rel L2 1e-3 and max-abs
+    5e-3 x max|ref| of the oracle's; rows with no key exactly -inf."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    empty = np.isneginf(ref)
+    assert (np.isneginf(got) == empty).all(), (what, got, ref)
+    if (~empty).any():
+        assert_close(got[~empty], ref[~empty], what + " lse")
+
+
+@pytest.mark.parametrize("kind", ["quant_splits", "quant_direct", "token_drop_none_kept", "identity_empty"])
+def test_draft_lse_and_empty_key_sets(kind):
+    """The optional lse output, on a call merged by the combine kernel
+    (many splits) and on a single-split call written directly; and compressed
+    parts that hold no row (no kept token, an empty identity cache) with tail
+    lengths 0, 5 and 33: the tail-only sequences match the oracle, the sequence
+    without any key gets o = 0 and lse = -inf."""
+    import torch
+    vc = _vc()
+    from compressed_kv_draft_amd.workload import bf16_dev
+    from synth.gen import f32_to_bf16_bits
+    print(f"[case] draft lse / empty key sets: {kind}", flush=True)
+    rng = np.random.default_rng({"quant_splits": 61, "quant_direct": 62}.get(kind, 63))
+    B, Hq, Hkv, D, T_cap = 3, 8, 2, 128, 40
+    g = Hq // Hkv
+    nq = 16384 if kind == "quant_splits" else (64 if kind == "quant_direct" else 96)
+    # quant_direct: two blocks and no tail, so one workgroup per (batch, kv-head) writes the output itself
+    lens = {"quant_splits": [7, 0, 40], "quant_direct": [0, 0, 0]}.get(kind, [0, 5, 33])
+    k = rng.standard_normal((B, Hkv, nq, D)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, nq, D)).astype(np.float32)
+    tk = rng.standard_normal((B, Hkv, T_cap, D)).astype(np.float32)
+    tv = rng.standard_normal((B, Hkv, T_cap, D)).astype(np.float32)
+    q = rng.standard_normal((B, Hq, D)).astype(np.float32)
+    kb, vb, tkb, tvb, qb = (f32_to_bf16_bits(x) for x in (k, v, tk, tv, q))
+    kd_, vd_ = bf16_dev(kb, "cuda"), bf16_dev(vb, "cuda")
+    if kind.startswith("quant"):
+        comp = vc.quantize_kv(kd_, vd_, 4, nq)
+    elif kind == "token_drop_none_kept":
+        comp = vc.token_drop_cache(kd_, vd_, torch.empty((B, Hkv, 0), dtype=torch.int32, device="cuda"))
+    else:
+        comp = vc.identity_cache(kd_, vd_, 0)
+    tail = vc.Tail() if kind == "quant_direct" else vc.Tail(
+        bf16_dev(tkb, "cuda"), bf16_dev(tvb, "cuda"), torch.tensor(lens, dtype=torch.int32, device="cuda"))
+    scale = O.scale_for(D)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    got = vc.draft_attn(comp, tail, bf16_dev(qb, "cuda"), scale, lse=lse).cpu().numpy()
+    got_lse = lse.cpu().numpy()
+    for b in range(B):
+        for h in range(Hkv):
+            qh = O.bf16_to_f64(qb[b, h * g:(h + 1) * g])
+            tail_k, tail_v = O.bf16_to_f64(tkb[b, h, :lens[b]]), O.bf16_to_f64(tvb[b, h, :lens[b]])
+            if kind.startswith("quant"):
+                kf = O.bf16_to_f64(kb[b, h]).astype(np.float32)
+                vf = O.bf16_to_f64(vb[b, h]).astype(np.float32)
+                keys, vals = O.draft_kv_rows("quant", k_deq=O.dequant_k(*O.quantize_k(kf, 4)),
+                                             v_deq=O.dequant_v(*O.quantize_v(vf, 4)), tail_k=tail_k, tail_v=tail_v)
+            elif kind == "token_drop_none_kept":
+                keys, vals = O.draft_kv_rows("token_drop", k_full=O.bf16_to_f64(kb[b, h]),
+                                             v_full=O.bf16_to_f64(vb[b, h]), keep_idx=np.zeros(0, np.int64),
+                                             tail_k=tail_k, tail_v=tail_v)
+            else:
+                keys, vals = O.draft_kv_rows("identity", k_full=O.bf16_to_f64(kb[b, h]),
+                                             v_full=O.bf16_to_f64(vb[b, h]), L=0, tail_k=tail_k, tail_v=tail_v)
+            what = f"{kind} b{b} h{h} ({len(keys)} keys)"
+            _assert_lse(got_lse[b, h * g:(h + 1) * g], O.draft_lse_unit(qh, keys, scale), what)
+            if len(keys):
+                assert_close(got[b, h * g:(h + 1) * g], O.draft_attention_unit(qh, keys, vals, scale), what)
+            else:
+                assert (got[b, h * g:(h + 1) * g] == 0).all(), what
+
+
 def test_verify_future_rows_do_not_leak():
     """Perturbing rows after L + j leaves verify position j bitwise unchanged."""
     from compressed_kv_draft_amd.workload import DeviceWorkload
