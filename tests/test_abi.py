@@ -97,6 +97,31 @@ def test_host_validation_without_gpu(lib):
     assert qb(None, None, 1, 1, 256, 128, 0, 1, ref, 0, None) == -1           # capacity not a multiple of 32
     d.kind = 2
     assert qb(None, None, 1, 1, 256, 128, 0, 1, ref, 0, None) == -1
+    # canonical <-> internal QUANT conversion: every check precedes the launch
+    pk, up = lib.vc_pack_quant, lib.vc_unpack_quant
+    pk.restype = up.restype = ctypes.c_int
+    q = Desc(kind=1, bits=4, n_quant=64, q_cap=128)
+    qr = ctypes.byref(q)
+    assert pk(None, None, None, None, 1, 1, 64, 128, None, 0, None) == -1      # null descriptor
+    assert up(None, 1, 1, 128, None, None, None, None, None) == -1
+    assert pk(None, None, None, None, 1, 1, 0, 128, qr, 4, None) == 0          # nothing to convert
+    assert pk(None, None, None, None, 1, 1, 64, 128, qr, 0, None) == -1        # null canonical arrays
+    assert b"null" in lib.vc_last_error()
+    assert pk(None, None, None, None, 1, 1, 48, 128, qr, 0, None) == -1        # rows not whole blocks
+    assert pk(None, None, None, None, 1, 1, 64, 128, qr, 3, None) == -1        # blocks past the capacity
+    assert b"outside" in lib.vc_last_error()
+    assert pk(None, None, None, None, 1, 1, 64, 96, qr, 0, None) == -2         # D=96 unsupported
+    assert pk(None, None, None, None, 0, 1, 64, 128, qr, 0, None) == -1        # B = 0
+    q.bits = 3
+    assert pk(None, None, None, None, 1, 1, 64, 128, qr, 0, None) == -1        # bits not 2 or 4
+    q.bits, q.kind = 4, 2
+    assert up(qr, 1, 1, 128, None, None, None, None, None) == -1               # not a QUANT cache
+    # workspace sizes: 0 for shapes no call accepts, a positive size otherwise
+    dw, vw = lib.vc_draft_ws_bytes, lib.vc_verify_ws_bytes
+    dw.restype = vw.restype = ctypes.c_size_t
+    assert dw(8, 32, 8, 128, 32768) >= 256 and dw(0, 32, 8, 128, 32768) == 0 and dw(8, 32, 8, 128, -1) == 0
+    assert vw(8, 32, 8, 128, 33, 32768) >= 256 and vw(8, 30, 8, 128, 33, 32768) == 0
+    assert vw(8, 32, 8, 128, 0, 32768) == 0
 
 
 def test_no_oracle_in_product_path():
